@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s (datasheet)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s (datasheet)
-DEFAULT_WORKLOAD = "prefill_4k"
+DEFAULT_WORKLOAD = "prefill_64k"
 COPY_MIB = 2048                # size of the calibration / measured-peak copy
 CSRC = os.path.join(ROOT, "dsa_lightning_indexer_02_amd", "csrc")
 # kernel source behind each stage (its hash marks which build a set of counters belongs to)
@@ -118,10 +118,13 @@ def _spread_order(n: int) -> list:
 def cpu_baseline(wl, seconds: float):
     """The oracle, as it stands, on a bounded row sample of the same workload (query tokens/s over the sample).
 
-    Rows are taken in an order whose every prefix spreads evenly over the batch, in chunks, until the time
-    budget is spent; all three steps run for each row (indexer row, its top-k, attention over that top-k)."""
+    Batches of more than 4096 rows (the 64K prefill) use a fixed stratified sample of 512 rows: 256 evenly spaced
+    and 256 seeded-random (workloads.stratified_rows, the rows its sampled parity test checks), all of them, and
+    report the measured time per row and the whole-batch time extrapolated from it. Smaller batches take rows in
+    an order whose every prefix spreads evenly over the batch until the time budget is spent. All three steps run
+    for each row (indexer row, its top-k, attention over that top-k)."""
     import oracle
-    from workloads import bits_u16, bits_u8
+    from workloads import bits_u16, bits_u8, stratified_rows
 
     model, blas, usable = _cpu_info()
     fp8 = wl.k_dtype == "fp8"
@@ -129,22 +132,27 @@ def cpu_baseline(wl, seconds: float):
               page_table=None if wl.page_table is None else wl.page_table.numpy(), page_size=wl.page_size)
     qidx, kidx = bits_u16(wl.q_idx), (bits_u8(wl.k_idx) if fp8 else bits_u16(wl.k_idx))
     q, lat = bits_u16(wl.q), bits_u16(wl.latent)
-    order = _spread_order(wl.n_q)
+    fixed = wl.n_q > 4096
+    order = [int(r) for r in stratified_rows(wl.n_q)] if fixed else _spread_order(wl.n_q)
     done, dt, chunk = 0, 0.0, 8
-    while done < len(order) and dt < seconds:
+    while done < len(order) and (fixed or dt < seconds):
         rows = sorted(order[done: done + chunk])
         t0 = time.perf_counter()
         sc = oracle.indexer_scores_rows(rows, q_idx=qidx, w=wl.w.numpy(), k_idx=kidx,
                                         k_scale=wl.k_scale.numpy() if fp8 else None, q_pos=wl.q_pos.numpy(), **kw)
-        idx = np.full((max(rows) + 1, wl.k), -1, dtype=np.int64)
-        for r, v in sc.items():
-            idx[r] = oracle.topk_select(v.astype(np.float32), wl.k)
+        idx = {r: oracle.topk_select(v.astype(np.float32), wl.k) for r, v in sc.items()}
         oracle.sparse_attn_rows(rows, q=q, latent=lat, idx=idx, sm_scale=wl.sm_scale, D_v=wl.D_v, **kw)
         dt += time.perf_counter() - t0
         done += len(rows)
-    return {"value": done / dt, "unit": "query tokens/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"{done} of {wl.n_q} query rows (spread evenly over the batch), all three steps, {dt:.1f} s; "
-                      f"numpy fp64, {blas} BLAS threads of {usable} usable cores, {model}"}
+    how = ("fixed stratified sample: 256 evenly spaced + 256 seeded-random rows" if fixed
+           else "rows spread evenly over the batch, until the time budget was spent")
+    rec = {"value": done / dt, "unit": "query tokens/s", "cores": int(blas), "kind": "oracle",
+           "sample": f"{done} of {wl.n_q} query rows ({how}), all three steps, {dt:.1f} s; "
+                     f"numpy fp64, {blas} BLAS threads of {usable} usable cores, {model}",
+           "per_row_ms": round(1e3 * dt / done, 3)}
+    if done < wl.n_q:
+        rec["extrapolated_full_batch_s"] = round(dt / done * wl.n_q, 1)   # an estimate, not a measurement
+    return rec
 
 
 def copy_calibration(reps: int = 5):
@@ -252,7 +260,15 @@ def main():
         traffic = None
     d = st[dom]
     roofline = {"bound": d["bound"], "achieved": round(d["achieved"], 3), "peak": d["peak"], "unit": d["unit"],
-                "frac": round(d["frac"], 4), "traffic": traffic, "kernel": dom}
+                "frac": round(d["frac"], 4), "traffic": traffic, "kernel": dom,
+                "launch_ms": round(stage_ms[dom], 4), "algorithmic": work[dom][1] if d["bound"] == "hbm" else work[dom][0]}
+    if traffic:
+        # the rate of the bytes that really crossed the L2/MALL boundary (rocprofv3 FETCH_SIZE + WRITE_SIZE), beside
+        # the algorithmic rate above: the two differ by the cache reuse of the gathered rows
+        roofline["measured_traffic_GBs"] = round(traffic / (stage_ms[dom] * 1e-3) / 1e9, 1)
+        roofline["measured_traffic_frac"] = round(traffic / (stage_ms[dom] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    if dom == "attention":
+        roofline["mfma_frac"] = round(st[dom]["mfma_frac"], 4)
 
     nxt = None if args.no_next_rows else next_rows(args, dsa, torch, wl, b, scores, idx, out, lse, tk_ws, at_ws,
                                                    stage_ms, stream)

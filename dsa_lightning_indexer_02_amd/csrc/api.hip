@@ -109,12 +109,19 @@ TopkPlan plan_topk(const dsa_batch *b, int k) {
   // the merge then has more candidates (measured on 64 x 32K and 16 x 16K..128K rows)
   int chunk = std::max(pow2_ceil(2LL * k), std::max(8192, pow2_ceil(ceil_div(L * b->num_q, 256))));
   while ((long long)b->num_q * ceil_div(L, chunk) > 2048 && chunk < 65536) chunk <<= 1;
-  chunk = std::max(chunk, pow2_ceil(ceil_div(L * k, 65536)));
+  // a chunk's keys and a row's candidates must fit one workgroup's registers (64 per thread): chunk <= 65536,
+  // and n_chunks * k <= 65536 (L * k / 65536 <= 65536 for L <= 2^20, k <= 4096)
+  chunk = std::max(std::min(chunk, 65536), pow2_ceil(ceil_div(L * k, 65536)));
   p.chunked = true;
   p.chunk = chunk;
   p.n_chunks = ceil_div(L, chunk);
   p.items_a = std::max(4, pow2_ceil(ceil_div(chunk, 1024)));
   p.items_b = pow2_ceil(ceil_div((long long)p.n_chunks * k, 1024));
+  if (p.items_a > 64 || p.items_b > 64) {   // no such register budget: one streaming workgroup per row instead
+    TopkPlan s{};
+    s.stream = true;
+    return s;
+  }
   p.ws_bytes = (size_t)b->num_q * p.n_chunks * k * 8;
   return p;
 }

@@ -1,6 +1,7 @@
 """Parity at the full 64K causal prefill (65,536 rows, 64 indexer heads, k = 2048, 16 needles per 4K block), in
-the launch configuration the benchmark times: each call runs over the whole batch, and sampled rows are
-checked against the oracle (MI355X only).
+the launch configuration the benchmark times: each call runs over the whole batch, and a fixed stratified sample of
+512 rows (256 evenly spaced + 256 seeded-random, the sample the benchmark times the oracle on) is checked
+against the oracle (MI355X only).
 
   indexer   the GPU scores of the sampled rows within the 1e-2 relative bar; entries past q_pos untouched;
   top-k     the oracle's fp32 scores are written into the sampled rows of the GPU score matrix, and dsa_topk
@@ -16,18 +17,19 @@ import torch
 
 import dsa_lightning_indexer_02_amd as dsa
 import oracle
-from workloads import make
+from workloads import make, stratified_rows
 
 from gpu_cases import DEV, attn_oracle, batch_of, bf16_to_f64, check_attn, indexer_rel_err, ld_for, oracle_scores, say
 
 pytestmark = pytest.mark.gpu
 
-ROWS = [0, 1, 2047, 2048, 2049, 4095, 4096, 20000, 32767, 49151, 65534, 65535]
+# the sample, plus the rows at the k boundary (the first rows that must select)
+ROWS = sorted(set(stratified_rows(65536).tolist()) | {1, 2047, 2048, 2049, 4095, 4096, 65534})
 
 
 def test_prefill_64k_sampled_rows():
     wl = make("prefill_64k")
-    say(f"[64k] n_q={wl.n_q} k={wl.k} sampled rows {ROWS}")
+    say(f"[64k] n_q={wl.n_q} k={wl.k} {len(ROWS)} sampled rows")
     d = wl.to(DEV)
     b = batch_of(d)
     ld = ld_for(wl.max_kv_len)
@@ -46,10 +48,11 @@ def test_prefill_64k_sampled_rows():
     assert worst <= 1.0
 
     # top-k over the whole batch, the sampled rows holding the oracle's fp32 scores
+    host = np.full((len(ROWS), ld), np.nan, dtype=np.float32)
     for i, r in enumerate(ROWS):
-        row = np.full(ld, np.nan, dtype=np.float32)
-        row[: len(ref[r])] = ref[r].astype(np.float32)
-        scores[r] = torch.from_numpy(row).to(DEV)
+        host[i, : len(ref[r])] = ref[r].astype(np.float32)
+    scores.index_copy_(0, rows_t, torch.from_numpy(host).to(DEV))
+    del host
     idx = dsa.topk(b, scores, wl.k)
     torch.cuda.synchronize()
     got_idx = idx.index_select(0, rows_t).cpu().numpy()
@@ -69,8 +72,7 @@ def test_prefill_64k_sampled_rows():
         say(f"  needles missed by the sampled rows' top-k: {missed}")
 
     # attention over the whole batch, the sampled rows holding the oracle's index lists
-    for r in ROWS:
-        idx[r] = torch.from_numpy(exp_idx[r].astype(np.int32)).to(DEV)
+    idx.index_copy_(0, rows_t, torch.from_numpy(np.stack([exp_idx[r] for r in ROWS]).astype(np.int32)).to(DEV))
     lse = torch.empty((wl.n_q, wl.H), dtype=torch.float32, device=DEV)
     n_ws = dsa.sparse_attn_workspace_size(b, wl.k, wl.H, wl.D_v)
     ws = torch.empty(max(n_ws, 16), dtype=torch.uint8, device=DEV) if n_ws else None

@@ -75,7 +75,8 @@ def test_dynamic_range_and_equal_rows():
     _run(s, pos, 2048, "dynamic range")
 
 
-@pytest.mark.parametrize("n_q,max_kv", [(64, 32768), (16, 131072), (3, 70000), (40, 5000)])
+@pytest.mark.parametrize("n_q,max_kv", [(64, 32768), (16, 131072), (3, 70000), (40, 5000), (300, 65536),
+                                        (256, 131072)])
 def test_chunked_two_pass(n_q, max_kv):
     rng = np.random.default_rng(n_q)
     s = _mk(n_q, max_kv, lambda n, g: np.abs(g.standard_normal(n)).astype(np.float32) * 0.1, rng)

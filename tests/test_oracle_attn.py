@@ -30,6 +30,29 @@ def _sdpa_causal(q, C, sm_scale, D_v):
     return o.permute(1, 0, 2).numpy()
 
 
+def _masked_dense_loops(q, C, sm_scale, D_v):
+    """Dense causal attention written out with scalar Python loops over a full score matrix: entries above the
+    diagonal are masked to -inf before a per-row softmax (max-subtracted exponentials over a plain sum).
+    q [L, H, D], C [L, D] -> out [L, H, D_v], lse [L, H]."""
+    L, H, D = q.shape
+    out = np.zeros((L, H, D_v))
+    lse = np.zeros((L, H))
+    for h in range(H):
+        z = [[-math.inf] * L for _ in range(L)]
+        for t in range(L):
+            for s in range(L):
+                if s <= t:
+                    z[t][s] = sm_scale * sum(float(q[t, h, d]) * float(C[s, d]) for d in range(D))
+        for t in range(L):
+            m = max(z[t])
+            e = [math.exp(v - m) if v != -math.inf else 0.0 for v in z[t]]
+            tot = sum(e)
+            for d in range(D_v):
+                out[t, h, d] = sum(e[s] * float(C[s, d]) for s in range(L)) / tot
+            lse[t, h] = m + math.log(tot)
+    return out, lse
+
+
 @pytest.mark.parametrize("peaky", [False, True])
 def test_k_at_least_context_equals_dense_causal(peaky):
     """With k >= p + 1 for every row, selection keeps every candidate and sparse attention is dense causal
@@ -41,11 +64,15 @@ def test_k_at_least_context_equals_dense_causal(peaky):
     C = rng.standard_normal((L, D)) * sc
     k = L + 3
     ref = _sdpa_causal(q, C, 1.0 / math.sqrt(D), Dv)
+    ref_loops, lse_loops = _masked_dense_loops(q, C, 1.0 / math.sqrt(D), Dv)
+    np.testing.assert_allclose(ref_loops, ref, rtol=1e-10, atol=1e-12)   # the two dense references agree
     for r in range(L):
         idx = topk_select(rng.standard_normal(r + 1).astype(np.float32), k)   # any scores: all are kept
         sel = idx[idx != -1]
         out, lse = sparse_attn(q[r], C[sel], 1.0 / math.sqrt(D), Dv)
         np.testing.assert_allclose(out, ref[r], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(out, ref_loops[r], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse, lse_loops[r], rtol=1e-12)
         # lse against the plain log-sum-exp of the causal row
         z = (q[r] @ C[: r + 1].T) / math.sqrt(D)
         np.testing.assert_allclose(lse, np.log(np.exp(z).sum(axis=1)), rtol=1e-12)

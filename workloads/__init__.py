@@ -10,6 +10,7 @@ from .gen import (  # noqa: F401
     make,
     make_prefill_batch,
     regen_rows,
+    stratified_rows,
     fp8_encode_rows,
     bits_u16,
     bits_u8,

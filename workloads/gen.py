@@ -339,6 +339,19 @@ def make_prefill_batch(seqs, *, seed: int = 11, base: str = "prefill_4k") -> Wor
         page_table=None, page_size=64, seq_stride=seq_stride)
 
 
+def stratified_rows(n: int, n_even: int = 256, n_rand: int = 256, seed: int = 0) -> np.ndarray:
+    """A fixed row sample of a batch of n query rows: n_even evenly spaced rows (both ends included) and n_rand
+    seeded uniform rows drawn without replacement from the rest; sorted, int64. For n <= n_even + n_rand it is
+    every row. The 64K prefill's oracle timing and its sampled parity check use the same sample."""
+    if n <= n_even + n_rand:
+        return np.arange(n, dtype=np.int64)
+    even = np.unique(np.round(np.linspace(0, n - 1, num=n_even)).astype(np.int64))
+    rest = np.setdiff1d(np.arange(n, dtype=np.int64), even)
+    rnd = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x5A, n]))).choice(
+        rest, size=n_rand, replace=False)
+    return np.sort(np.concatenate([even, rnd]))
+
+
 def regen_rows(name: str, tensor: str, rows, *, peaky: bool = False) -> torch.Tensor:
     """Regenerate selected query rows of `tensor` in {"q_idx", "w", "q"} exactly as make() draws them."""
     cfg = dict(CONFIGS[name])
