@@ -28,6 +28,7 @@ __all__ = [
     "indexer_scores",
     "topk",
     "topk_workspace_size",
+    "topk_noalloc",
     "sparse_attn",
     "sparse_attn_workspace_size",
     "cache_append",
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_topk_workspace_size.argtypes = [BP, I32, ctypes.POINTER(SZ)]
     L.dsa_topk.restype = ctypes.c_int
     L.dsa_topk.argtypes = [BP, P, I64, I32, P, P, SZ, P]
+    L.dsa_topk_noalloc.restype = ctypes.c_int
+    L.dsa_topk_noalloc.argtypes = [BP, P, I64, I32, P, P]
     L.dsa_sparse_attn_workspace_size.restype = ctypes.c_int
     L.dsa_sparse_attn_workspace_size.argtypes = [BP, I32, I32, I32, ctypes.POINTER(SZ)]
     L.dsa_sparse_attn.restype = ctypes.c_int
@@ -219,6 +222,15 @@ def topk(batch: Batch, scores: torch.Tensor, k: int, idx: Optional[torch.Tensor]
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().dsa_topk(batch.c, _ptr(scores), int(scores.stride(0)), int(k), _ptr(idx), _ptr(ws), nbytes,
                           _stream()))
+    return idx
+
+
+def topk_noalloc(batch: Batch, scores: torch.Tensor, k: int, idx: torch.Tensor) -> torch.Tensor:
+    """dsa_topk_noalloc: the same selection as topk, using the library's own scratch array instead of a workspace
+    (no allocation in the call; idx must be given). Returns idx."""
+    _need(scores, "scores", torch.float32, 2)
+    _need(idx, "idx", torch.int32, 2)
+    _check(lib().dsa_topk_noalloc(batch.c, _ptr(scores), int(scores.stride(0)), int(k), _ptr(idx), _stream()))
     return idx
 
 

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "dsa.h"
@@ -139,6 +140,51 @@ int plan_attn_splits(const dsa_batch *b, int k) {
   return std::max(need, std::min(cap, std::max(1, ceil_div(256, std::max(1, b->num_q)))));
 }
 
+// Launches of dsa_topk's plan (arguments already checked; ws holds the plan's workspace bytes).
+dsa_status topk_launch(const dsa_batch *b, const float *scores, int64_t ld_scores, int32_t k, int32_t *idx, void *ws,
+                       hipStream_t stream) {
+  const TopkPlan p = plan_topk(b, k);
+  hipError_t e;
+  if (p.stream) {
+    e = dsa::launch_topk_stream(scores, ld_scores, b->q_pos, b->num_q, k, idx, stream);
+  } else if (!p.chunked) {
+    e = dsa::launch_topk_rows(scores, ld_scores, b->q_pos, b->num_q, k, idx, p.items_a, stream);
+  } else {
+    uint32_t *ck = static_cast<uint32_t *>(ws);
+    int32_t *cp = reinterpret_cast<int32_t *>(ck + (size_t)b->num_q * p.n_chunks * k);
+    e = dsa::launch_topk_chunked(scores, ld_scores, b->q_pos, b->num_q, k, p.chunk, p.n_chunks, ck, cp, idx,
+                                 p.items_a, p.items_b, stream);
+  }
+  return from_hip(e, "dsa_topk launch");
+}
+
+// ---- the no-allocation top-k: its workspace is this file-scope device array. In host code `scratch` names a
+// host-side stand-in, not device memory: kernels and copies get the address hipGetSymbolAddress reports, taken
+// once per device with that device current (each device holds its own copy of the array).
+constexpr size_t kNoallocScratchBytes = DSA_TOPK_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+dsa_status scratch_of_current_device(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "dsa_topk_noalloc: hipGetDevice");
+  DSA_CHECK(dev >= 0 && dev < kMaxDevices, DSA_ERR_UNSUPPORTED, "dsa_topk_noalloc: device %d (at most %d devices)",
+            dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return from_hip(e, "dsa_topk_noalloc: hipGetSymbolAddress");
+    DSA_CHECK(p != nullptr, DSA_ERR_HIP, "dsa_topk_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,19 +271,28 @@ dsa_status dsa_topk(const dsa_batch *b, const float *scores, int64_t ld_scores, 
   DSA_CHECK(ws_bytes >= need && (need == 0 || ws != nullptr), DSA_ERR_WORKSPACE,
             "top-k needs %zu bytes of workspace (got %zu)", need, ws_bytes);
   DSA_CHECK(need == 0 || aligned(ws, 16), DSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-  const TopkPlan p = plan_topk(b, k);
-  hipError_t e;
-  if (p.stream) {
-    e = dsa::launch_topk_stream(scores, ld_scores, b->q_pos, b->num_q, k, idx, (hipStream_t)stream);
-  } else if (!p.chunked) {
-    e = dsa::launch_topk_rows(scores, ld_scores, b->q_pos, b->num_q, k, idx, p.items_a, (hipStream_t)stream);
-  } else {
-    uint32_t *ck = static_cast<uint32_t *>(ws);
-    int32_t *cp = reinterpret_cast<int32_t *>(ck + (size_t)b->num_q * p.n_chunks * k);
-    e = dsa::launch_topk_chunked(scores, ld_scores, b->q_pos, b->num_q, k, p.chunk, p.n_chunks, ck, cp, idx,
-                                 p.items_a, p.items_b, (hipStream_t)stream);
+  return topk_launch(b, scores, ld_scores, k, idx, ws, (hipStream_t)stream);
+}
+
+dsa_status dsa_topk_noalloc(const dsa_batch *b, const float *scores, int64_t ld_scores, int32_t k, int32_t *idx,
+                            void *stream) {
+  size_t need = 0;
+  dsa_status st = dsa_topk_workspace_size(b, k, &need);
+  if (st != DSA_OK) return st;
+  DSA_CHECK(need <= kNoallocScratchBytes, DSA_ERR_UNSUPPORTED,
+            "dsa_topk_noalloc: this batch needs %zu bytes of scratch; the library holds %zu (use dsa_topk with a "
+            "workspace)", need, kNoallocScratchBytes);
+  DSA_CHECK(ld_scores >= b->max_kv_len, DSA_ERR_INVALID_ARGUMENT, "ld_scores (%lld) must be >= max_kv_len (%d)",
+            (long long)ld_scores, b->max_kv_len);
+  if (b->num_q == 0) return ok();
+  DSA_CHECK(scores && idx, DSA_ERR_INVALID_ARGUMENT, "scores and idx must be non-NULL");
+  DSA_CHECK(aligned(scores, 16) && aligned(idx, 16), DSA_ERR_INVALID_ARGUMENT, "scores / idx must be 16-byte aligned");
+  void *ws = nullptr;
+  if (need > 0) {
+    st = scratch_of_current_device(&ws);
+    if (st != DSA_OK) return st;
   }
-  return from_hip(e, "dsa_topk launch");
+  return topk_launch(b, scores, ld_scores, k, idx, ws, (hipStream_t)stream);
 }
 
 dsa_status dsa_sparse_attn_workspace_size(const dsa_batch *b, int32_t k, int32_t H, int32_t D_v, size_t *bytes) {

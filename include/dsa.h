@@ -21,8 +21,9 @@
  * Conventions shared by every call
  *   - Every tensor argument is a caller-owned DEVICE pointer to row-major, densely packed data unless a
  *     leading dimension is given. libdsa allocates no device memory, keeps no pointer after it returns and
- *     holds no global mutable state: calls are reentrant. Buffers must stay alive until the stream has run
- *     the kernels. Outputs must not alias inputs.
+ *     holds no global mutable state: calls are reentrant. (The one exception is dsa_topk_noalloc, which uses
+ *     a device array the library holds; see there.) Buffers must stay alive until the stream has run the
+ *     kernels. Outputs must not alias inputs.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream). Every call is asynchronous on it.
  *   - All argument checks run on the host, before any launch. A call that fails a check launches nothing
  *     and returns a non-zero dsa_status; dsa_last_error() then gives a message for the calling thread.
@@ -130,6 +131,21 @@ dsa_status dsa_topk_workspace_size(const dsa_batch *b, int32_t k, size_t *bytes)
  */
 dsa_status dsa_topk(const dsa_batch *b, const float *scores, int64_t ld_scores, int32_t k, int32_t *idx,
                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dsa_topk_noalloc — dsa_topk for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Same arguments, rules and result as dsa_topk, without the
+ * workspace: the plans that need one (few rows over long contexts, e.g. decode batches) use a device array the
+ * library holds, DSA_TOPK_NOALLOC_SCRATCH_BYTES per GPU, from the first call on that GPU until the process ends.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library routine); it resolves the array's
+ * device address once per device, on the calling thread's current device, which must be the stream's device.
+ *   A batch whose dsa_topk_workspace_size exceeds DSA_TOPK_NOALLOC_SCRATCH_BYTES: DSA_ERR_UNSUPPORTED, nothing
+ *   launched. Every call on one GPU shares that GPU's array and nothing in it must start at any value (each call
+ *   writes the parts it reads), but calls that overlap on one GPU (other streams, other threads) race on it.
+ */
+#define DSA_TOPK_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+dsa_status dsa_topk_noalloc(const dsa_batch *b, const float *scores, int64_t ld_scores, int32_t k, int32_t *idx,
+                            void *stream);
 
 /* Bytes of device workspace dsa_sparse_attn needs for this batch and shape (may be 0). */
 dsa_status dsa_sparse_attn_workspace_size(const dsa_batch *b, int32_t k, int32_t H, int32_t D_v,
