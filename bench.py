@@ -9,6 +9,7 @@ the same workload.
 
 Profiling helpers (same file, so every profile is made by committed code):
   python bench.py --copy-calibration        a plain device copy of known size, for scaling the HBM counters
+  python bench.py --profile-commands DIR    the rocprofv3 passes behind the profiles/ summaries (output under DIR)
   python bench.py --ingest-profiles DIR     turn the rocprofv3 output under DIR into summaries in profiles/
 """
 
@@ -54,6 +55,8 @@ def parse():
                     help="per-kernel HBM bytes from rocprofv3 counters (JSON), if present")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ingest-profiles", metavar="DIR")
+    ap.add_argument("--profile-commands", metavar="DIR",
+                    help="print the rocprofv3 commands of the workload's profile passes (output under DIR), one a line")
     return ap.parse_args()
 
 
@@ -178,6 +181,10 @@ def main():
     args = parse()
     if args.ingest_profiles:
         ingest_profiles(args.ingest_profiles, args.workload)
+        return
+    if args.profile_commands:
+        for c in profile_commands(args.workload).values():
+            print(c.replace("DIR", os.path.abspath(args.profile_commands)).replace("$R", ROOT))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path; "
@@ -412,18 +419,35 @@ def next_rows(args, dsa, torch, wl, b, scores, idx, out, lse, tk_ws, at_ws, stag
 # ---------------------------------------------------------------------------------------------------------------
 # rocprofv3 output -> profiles/ summaries (run on any machine; reads CSV files only)
 
+# Counter passes (rocprofv3 collects at most 8 SQ_ and 2 GRBM_ counters in one pass; each pass is its own run).
+# MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCC * 4 SIMDs * 256 CUs), the expression of
+# rocprofv3's own MfmaUtil metric, which the third pass collects for comparison together with LDSBankConflict.
+COUNTER_PASSES = {
+    "sq_issue": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD",
+                 "SQ_INSTS_SALU", "SQ_WAVES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "GRBM_COUNT"],
+    "sq_lds": ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+               "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+               "GRBM_GUI_ACTIVE"],
+    "derived": ["MfmaUtil", "LDSBankConflict"],
+}
+N_XCC, N_CU, N_SIMD = 8, 256, 1024
+
+
 def profile_commands(workload: str) -> dict:
     """The rocprofv3 commands whose output --ingest-profiles reads, run from the repository root on the MI355X machine
     (after `cd /tmp && export TMPDIR=/tmp`, with R the repository root; each pass is its own process)."""
     b = f"python3 $R/bench.py --workload {workload} --steps 5 --warmup 2 --no-cpu-baseline --no-next-rows"
     c = "python3 $R/bench.py --copy-calibration"
-    return {
+    cmds = {
         "ktrace": f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/ktrace -o run -- {b}",
         "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- {b}",
         "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o run -- {b}",
         "cal_fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/cal_fetch -o run -- {c}",
         "cal_write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/cal_write -o run -- {c}",
     }
+    for name, ctrs in COUNTER_PASSES.items():
+        cmds[name] = f"rocprofv3 --pmc {' '.join(ctrs)} --output-format csv -d DIR/{name} -o run -- {b}"
+    return cmds
 
 
 def _read_csv(pattern):
@@ -486,7 +510,8 @@ def ingest_profiles(d: str, workload: str):
     cf = _counter_per_dispatch(_read_csv(os.path.join(d, "cal_fetch", "**", "*counter_collection.csv")), "FETCH_SIZE")
     cw = _counter_per_dispatch(_read_csv(os.path.join(d, "cal_write", "**", "*counter_collection.csv")), "WRITE_SIZE")
     if not (fetch and write and cf and cw):
-        print("no counter files found; kernel-trace summaries only", file=sys.stderr)
+        print("no FETCH_SIZE / WRITE_SIZE files found; no traffic summary", file=sys.stderr)
+        ingest_counters(d, workload, cmds, stats)
         return
     copy_bytes = COPY_MIB << 20
     # the copy kernel is the one whose counters are largest in the calibration runs
@@ -520,6 +545,76 @@ def ingest_profiles(d: str, workload: str):
     with open(os.path.join(out_dir, f"hbm_traffic_{workload}.md"), "w") as f:
         f.write("\n".join(txt) + "\n")
     print(f"wrote {path} and summaries in {out_dir}")
+    ingest_counters(d, workload, cmds, stats)
+
+
+def _per_dispatch(rows):
+    """{kernel: {counter: mean per dispatch}} and {kernel: mean duration ns under counter collection}."""
+    acc, dur = {}, {}
+    for r in rows:
+        k = r["Kernel_Name"]
+        acc.setdefault(k, {}).setdefault(r["Counter_Name"], {})
+        d = acc[k][r["Counter_Name"]]
+        d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        dur.setdefault(k, {})[r["Dispatch_Id"]] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return ({k: {c: float(np.mean(list(v.values()))) for c, v in cs.items()} for k, cs in acc.items()},
+            {k: float(np.mean(list(v.values()))) for k, v in dur.items()})
+
+
+def ingest_counters(d: str, workload: str, cmds: dict, stats):
+    """profiles/counters_<workload>.md: per-kernel SQ counters of the indexer, top-k and attention kernels."""
+    per, dur = {}, {}
+    for name in COUNTER_PASSES:
+        rows = _read_csv(os.path.join(d, name, "**", "*counter_collection.csv"))
+        p, t = _per_dispatch(rows)
+        for k, cs in p.items():
+            per.setdefault(k, {}).update(cs)
+        for k, v in t.items():
+            dur.setdefault(k, []).append(v)
+    if not per:
+        print("no SQ counter files found", file=sys.stderr)
+        return
+    trace_ns = {r["Name"]: float(r["AverageNs"]) for r in stats}
+    txt = [f"# SQ counters per launch, workload {workload}: MFMA utilisation, instruction mix, LDS bank conflicts", "",
+           "Commands (from the repository root, R = its path; `cd /tmp && export TMPDIR=/tmp` first; one pass each):", ""]
+    txt += [f"    {cmds[n].replace('DIR', d.rstrip('/'))}" for n in COUNTER_PASSES]
+    txt += ["", "Derived here, per launch (counter values are summed over the chip by rocprofv3):",
+            f"- clock = GRBM_GUI_ACTIVE / {N_XCC} XCDs / the kernel-trace average duration;",
+            f"- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {N_XCC} x {N_SIMD} SIMDs), rocprofv3's MfmaUtil "
+            "expression (its own MfmaUtil value is listed beside it);",
+            "- MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512;",
+            "- LDS bank-conflict cycles per LDS-active cycle = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE;",
+            "- instructions per wave = SQ_INSTS_* / SQ_WAVES.", ""]
+    hdr = ("| kernel | trace µs | clock GHz | MFMA busy (MfmaUtil) | MFMA TFLOP/s | MFMA / VALU / LDS / VMEM-rd / SALU "
+           "instr per wave | LDS conflict cycles / LDS-active cycles (LDSBankConflict) | wait-any / active-any |")
+    txt += [hdr, "|---|---|---|---|---|---|---|---|"]
+    for k in sorted(per, key=lambda x: -trace_ns.get(x, 0.0)):
+        stage = _stage_of(k)
+        if stage is None:
+            continue
+        c = per[k]
+        t_ns = trace_ns.get(k) or float(np.mean(dur.get(k, [0.0])))
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0) / N_XCC
+        clk = gui / t_ns if t_ns else 0.0
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * N_SIMD) if gui else 0.0
+        flops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        waves = max(c.get("SQ_WAVES", 1.0), 1.0)
+        mix = " / ".join(f"{c.get(x, 0.0) / waves:.0f}" for x in
+                         ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU"))
+        lds = c.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(c.get("SQ_LDS_IDX_ACTIVE", 0.0), 1.0)
+        wait = c.get("SQ_WAIT_INST_ANY", 0.0) / max(c.get("SQ_ACTIVE_INST_ANY", 0.0), 1.0)
+        txt.append(f"| `{k.split('(')[0][:70]}` | {t_ns / 1e3:.2f} | {clk:.2f} | {100 * busy:.1f} % "
+                   f"({c.get('MfmaUtil', float('nan')):.1f} %) | {flops / (t_ns * 1e-9) / 1e12 if t_ns else 0:.0f} "
+                   f"| {mix} | {lds:.4f} ({c.get('LDSBankConflict', float('nan')):.2f} %) | {wait:.2f} |")
+    txt += ["", "Raw counter means per launch:", "", "| kernel | counter | value |", "|---|---|---|"]
+    for k in sorted(per):
+        if _stage_of(k) is None:
+            continue
+        for cn, v in sorted(per[k].items()):
+            txt.append(f"| `{k.split('(')[0][:50]}` | {cn} | {v:.6g} |")
+    with open(os.path.join(ROOT, "profiles", f"counters_{workload}.md"), "w") as f:
+        f.write("\n".join(txt) + "\n")
+    print(f"wrote profiles/counters_{workload}.md")
 
 
 if __name__ == "__main__":

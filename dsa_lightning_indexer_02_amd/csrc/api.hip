@@ -86,11 +86,12 @@ dsa::SlotMap slot_map(const dsa_batch *b) {
 
 // ---- top-k plan: batches that fill the GPU take one workgroup per row, rows of at least
 //      kTopkStreamMinLen through the streaming form (sampled window, nothing held in registers) and shorter
-//      ones held in registers; otherwise chunks of each row keep their own top-k and a second pass merges.
+//      ones held in registers; otherwise (few rows: decode) each row splits into chunks that keep only the keys
+//      of a sampled window, and a merge pass selects among them (the windowed form).
 constexpr long long kTopkStreamMinLen = 8192;
 struct TopkPlan {
-  bool chunked, stream;
-  int items_a, items_b, chunk, n_chunks;
+  bool windowed, stream;
+  int items_a, chunk, n_chunks;
   size_t ws_bytes;
 };
 
@@ -102,28 +103,16 @@ TopkPlan plan_topk(const dsa_batch *b, int k) {
     return p;
   }
   if ((L <= 65536 && b->num_q >= 512) || L <= k) {
-    p.chunked = false;
     p.items_a = pow2_ceil(ceil_div(L, 1024));
     return p;
   }
-  // about 256 chunk workgroups in all: more of them each select too little to pay for their fixed cost, and
-  // the merge then has more candidates (measured on 64 x 32K and 16 x 16K..128K rows)
-  int chunk = std::max(pow2_ceil(2LL * k), std::max(8192, pow2_ceil(ceil_div(L * b->num_q, 256))));
-  while ((long long)b->num_q * ceil_div(L, chunk) > 2048 && chunk < 65536) chunk <<= 1;
-  // a chunk's keys and a row's candidates must fit one workgroup's registers (64 per thread): chunk <= 65536,
-  // and n_chunks * k <= 65536 (L * k / 65536 <= 65536 for L <= 2^20, k <= 4096)
-  chunk = std::max(std::min(chunk, 65536), pow2_ceil(ceil_div(L * k, 65536)));
-  p.chunked = true;
+  // about 256 chunk workgroups in all (chunks of 4096, 8192 or 16384 keys, one 256-thread workgroup each, at most
+  // 256 per row: L <= 2^20 needs at most 64)
+  const int chunk = std::min(16384, std::max(4096, pow2_ceil(ceil_div(L * b->num_q, 256))));
+  p.windowed = true;
   p.chunk = chunk;
   p.n_chunks = ceil_div(L, chunk);
-  p.items_a = std::max(4, pow2_ceil(ceil_div(chunk, 1024)));
-  p.items_b = pow2_ceil(ceil_div((long long)p.n_chunks * k, 1024));
-  if (p.items_a > 64 || p.items_b > 64) {   // no such register budget: one streaming workgroup per row instead
-    TopkPlan s{};
-    s.stream = true;
-    return s;
-  }
-  p.ws_bytes = (size_t)b->num_q * p.n_chunks * k * 8;
+  p.ws_bytes = dsa::topk_windowed_ws_bytes(b->num_q, p.n_chunks, std::min(k, chunk));
   return p;
 }
 
@@ -147,13 +136,10 @@ dsa_status topk_launch(const dsa_batch *b, const float *scores, int64_t ld_score
   hipError_t e;
   if (p.stream) {
     e = dsa::launch_topk_stream(scores, ld_scores, b->q_pos, b->num_q, k, idx, stream);
-  } else if (!p.chunked) {
+  } else if (!p.windowed) {
     e = dsa::launch_topk_rows(scores, ld_scores, b->q_pos, b->num_q, k, idx, p.items_a, stream);
   } else {
-    uint32_t *ck = static_cast<uint32_t *>(ws);
-    int32_t *cp = reinterpret_cast<int32_t *>(ck + (size_t)b->num_q * p.n_chunks * k);
-    e = dsa::launch_topk_chunked(scores, ld_scores, b->q_pos, b->num_q, k, p.chunk, p.n_chunks, ck, cp, idx,
-                                 p.items_a, p.items_b, stream);
+    e = dsa::launch_topk_windowed(scores, ld_scores, b->q_pos, b->num_q, k, p.chunk, p.n_chunks, ws, idx, stream);
   }
   return from_hip(e, "dsa_topk launch");
 }

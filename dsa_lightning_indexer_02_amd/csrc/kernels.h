@@ -34,9 +34,9 @@ hipError_t launch_topk_rows(const float *scores, int64_t ld, const int32_t *q_po
                             int32_t *idx, int items, hipStream_t s);
 hipError_t launch_topk_stream(const float *scores, int64_t ld, const int32_t *q_pos, int num_q, int k, int32_t *idx,
                               hipStream_t s);
-hipError_t launch_topk_chunked(const float *scores, int64_t ld, const int32_t *q_pos, int num_q, int k, int chunk,
-                               int n_chunks, uint32_t *cand_key, int32_t *cand_pos, int32_t *idx, int items_a,
-                               int items_b, hipStream_t s);
+hipError_t launch_topk_windowed(const float *scores, int64_t ld, const int32_t *q_pos, int num_q, int k, int chunk,
+                                int n_chunks, void *ws, int32_t *idx, hipStream_t s);
+size_t topk_windowed_ws_bytes(int num_q, int n_chunks, int cap);
 
 struct AttnArgs {
   const void *q;            // [num_q, H, D_qk] bf16

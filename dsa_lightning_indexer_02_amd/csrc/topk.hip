@@ -13,10 +13,8 @@
 //      number of T-valued keys still to take are known;
 //   3. ordered compaction: wave ballots give per-(item, wave) counts, one block scan of those counts gives
 //      every selected element its output slot in position order, so the output is ascending with no sort.
-// Rows longer than one workgroup's register capacity, and batches with too few rows to fill the GPU, are
-// split into chunks: each chunk keeps its own top-k (the global top-k of a row is contained in the union
-// of its chunks' top-k under the same total order), and a second pass selects k among the candidates,
-// which are stored in position order.
+// Batches with too few rows to fill the GPU (decode) split each row into chunks that keep only the keys of a
+// sampled window (windowed form below), and a second pass selects k among those candidates.
 #include "common.h"
 #include "kernels.h"
 #include "topk_select.h"
@@ -46,37 +44,9 @@ __global__ __launch_bounds__(kTopkBlock) void topk_rows_kernel(const float *__re
   select_topk<ITEMS>(key, n, k, [&](int rank, int L, uint32_t) { out[rank] = L; }, sh);
 }
 
-// Pass 1 of the chunked form: chunk c of row r keeps its own top-k (or all of it when shorter), written
-// in position order as (key, position) candidates at slot (r * n_chunks + c) * k.
-template <int ITEMS>
-__global__ __launch_bounds__(kTopkBlock) void topk_chunk_kernel(const float *__restrict__ scores, int64_t ld,
-                                                               const int32_t *__restrict__ q_pos, int k,
-                                                               int chunk, int n_chunks,
-                                                               uint32_t *__restrict__ cand_key,
-                                                               int32_t *__restrict__ cand_pos) {
-  __shared__ TopkShared sh;
-  const int r = blockIdx.x, c = blockIdx.y;
-  const int n = q_pos[r] + 1;
-  if (n <= k) return;  // the merge pass writes such rows directly
-  const int start = c * chunk;
-  if (start >= n) return;
-  const int len = min(chunk, n - start);
-  const float *row = scores + (int64_t)r * ld + start;
-  const int64_t dst = ((int64_t)r * n_chunks + c) * k;
-  uint32_t key[ITEMS];
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int L = i * kTopkBlock + threadIdx.x;
-    key[i] = L < len ? order_key(row[L]) : 0u;
-  }
-  select_topk<ITEMS>(key, len, k, [&](int rank, int L, uint32_t kk) {
-    cand_key[dst + rank] = kk;
-    cand_pos[dst + rank] = start + L;
-  }, sh);
-}
-
-// Pass 2: select k among the row's candidates. Chunks before the last one each hold exactly k
-// candidates (chunk >= k), so the candidates of a row are contiguous and in position order.
+// Merge of the fused indexer -> top-k: select k among the row's candidates, chunk c's own top-k at slot
+// (r * n_chunks + c) * k. Chunks before the last one each hold exactly k candidates (chunk >= k), so the
+// candidates of a row are contiguous and in position order.
 template <int ITEMS>
 __global__ __launch_bounds__(kTopkBlock) void topk_merge_kernel(const int32_t *__restrict__ q_pos, int k,
                                                                int chunk, int n_chunks,
@@ -114,8 +84,9 @@ __global__ __launch_bounds__(kTopkBlock) void topk_merge_kernel(const int32_t *_
 //   2. one pass over the row keeps every key >= lo, with its position, in the wave's LDS region (in position
 //      order), and counts the keys above the window (16-byte loads, 4 positions per lane, when the rows are
 //      16-byte aligned);
-//   3. a bucket search over the window's keys in LDS finds the exact threshold T and how many T-valued keys
-//      are taken (lowest positions first); each wave then writes its kept positions from LDS, in order.
+//   3. a bucket search over the window's keys (each lane's share of its wave's LDS region loaded into registers
+//      once) finds the exact threshold T and how many T-valued keys are taken (lowest positions first); each
+//      wave then writes its kept positions, in order.
 // The row is read from HBM once. When the window misses the k-th key, or a wave's keys overflow its region,
 // a streaming bucket select over the whole row finds T instead (three passes of 11, 11 and 10 key bits),
 // followed by a counting pass and an output pass.
@@ -186,72 +157,6 @@ __device__ __forceinline__ void stream_rank_bins(StreamShared &sh, const int (&r
 
 __device__ __forceinline__ void stream_clear_hist(StreamShared &sh) {
   for (int b = threadIdx.x; b < kBins; b += kStreamThreads) sh.hist[b] = 0u;
-}
-
-// Exact threshold among the keys held in LDS (wave v's region holds cnt[v] keys; 1 <= need <= their total):
-// the need-th largest key T, the count of keys equal to T, and how many of those are taken.
-// (the window's keys are the candidates of each wave's region that are <= top)
-__device__ __forceinline__ bool lds_key(const StreamShared &sh, const uint32_t (&cnt)[kStreamWaves], uint32_t top,
-                                        int i, uint32_t &x) {
-  const int v = i / kCandPerWave, j = i - v * kCandPerWave;
-  x = sh.cand_key[i];
-  return (uint32_t)j < cnt[v] && x <= top;
-}
-__device__ __forceinline__ void lds_threshold(StreamShared &sh, const uint32_t (&cnt)[kStreamWaves], uint32_t top,
-                                              uint32_t need, uint32_t &T, uint32_t &need_eq, uint32_t &cnt_eq) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (int i = tid; i < kStreamWaves * kCandPerWave; i += kStreamThreads) {
-    uint32_t x;
-    if (lds_key(sh, cnt, top, i, x)) {
-      kmin = min(kmin, x);
-      kmax = max(kmax, x);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-  }
-  if (lane == 0) {
-    sh.red[w] = kmin;
-    sh.red[kStreamWaves + w] = kmax;
-  }
-  __syncthreads();
-  kmin = sh.red[0];
-  kmax = sh.red[kStreamWaves];
-#pragma unroll
-  for (int i = 1; i < kStreamWaves; ++i) {
-    kmin = min(kmin, sh.red[i]);
-    kmax = max(kmax, sh.red[kStreamWaves + i]);
-  }
-  uint32_t lo = kmin, hi = kmax;
-  const uint32_t range = kmax - kmin;
-  int shift = range == 0u ? 0 : max(0, 32 - __clz((int)range) - kBinBits);
-  while (true) {
-    __syncthreads();
-    stream_clear_hist(sh);
-    __syncthreads();
-    for (int i = tid; i < kStreamWaves * kCandPerWave; i += kStreamThreads) {
-      uint32_t x;
-      if (lds_key(sh, cnt, top, i, x) && x >= lo && x <= hi) atomicAdd(&sh.hist[(x - lo) >> shift], 1u);
-    }
-    __syncthreads();
-    const int rr[1] = {(int)need};
-    stream_rank_bins<1>(sh, rr);
-    const uint32_t B = sh.bcast[0], above = sh.bcast[1], inbin = sh.bcast[2];
-    need -= above;
-    lo += B << shift;
-    hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + ((1ull << shift) - 1ull));
-    if (shift == 0) {
-      T = lo;
-      cnt_eq = inbin;
-      need_eq = need;
-      break;
-    }
-    shift = max(0, shift - kBinBits);
-  }
-  __syncthreads();
 }
 
 // The k-th largest key of the whole row by streaming bucket passes over the row (exact; used when the sampled
@@ -343,25 +248,11 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return v;
 }
 
-__global__ __launch_bounds__(kStreamThreads) void topk_stream_kernel(const float *__restrict__ scores, int64_t ld,
-                                                                     const int32_t *__restrict__ q_pos, int num_q,
-                                                                     int k, int32_t *__restrict__ idx) {
-  __shared__ StreamShared sh;
-  const int r = num_q - 1 - (int)blockIdx.x;    // longest rows of a prefill first
-  const int n = q_pos[r] + 1;
-  int32_t *out = idx + (int64_t)r * k;
+// ---- 1. sample: run b (0..63) starts at floor(b * (n - 64) / 63); wave w reads runs 16w .. 16w+15. Gives the
+//      window [lo, hi] (lo = 0 / hi = ~0 when the margin reaches past the sample). Uses hist, red, bcast.
+__device__ __forceinline__ void stream_window(const float *__restrict__ row, int n, int k, StreamShared &sh,
+                                              uint32_t &lo, uint32_t &hi) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  if (n <= k) {
-    for (int j = tid; j < k; j += kStreamThreads) out[j] = j < n ? j : -1;
-    return;
-  }
-  const float *row = scores + (int64_t)r * ld;
-  // segments start at multiples of 256 positions, so 16-byte aligned when the row is
-  const int seg = ((n + kStreamWaves - 1) / kStreamWaves + 4 * kWave - 1) / (4 * kWave) * (4 * kWave);
-  const bool vec = (ld & 3) == 0 && ((uintptr_t)scores & 15) == 0;
-  const int s0 = min(n, w * seg), s1 = min(n, s0 + seg);
-
-  // ---- 1. sample: run b (0..63) starts at floor(b * (n - 64) / 63); wave w reads runs 16w .. 16w+15
   constexpr int SP = kSample / kStreamThreads;
   uint32_t sk[SP];
 #pragma unroll
@@ -408,16 +299,25 @@ __global__ __launch_bounds__(kStreamThreads) void topk_stream_kernel(const float
     const int rr[2] = {max(1, min(kSample, r_hi + 1)), max(1, min(kSample, r_lo))};
     stream_rank_bins<2>(sh, rr);
   }
-  uint32_t hi = 0xffffffffu, lo = 0u;
+  hi = 0xffffffffu;
+  lo = 0u;
   if (r_hi >= 0 && r_hi + 1 <= kSample)
     hi = (uint32_t)min((uint64_t)0xffffffffu, (uint64_t)smin + ((uint64_t)(sh.bcast[0] + 1) << shift) - 1ull);
   if (r_lo <= kSample) lo = smin + (sh.bcast[3] << shift);
+}
 
-  // ---- 2. one pass: keep every key >= lo with its position (position order), count the keys above hi
+// ---- 2. one pass over this wave's segment [s0, s1): every key >= lo with its position goes to the wave's LDS
+//      region (position order; cc counts them all, only the first kCandPerWave are stored), and ca counts the
+//      keys above hi.
+__device__ __forceinline__ void stream_collect(const float *__restrict__ row, int s0, int s1, bool vec, uint32_t lo,
+                                               uint32_t hi, StreamShared &sh, uint32_t &ca, uint32_t &cc) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int cb = w * kCandPerWave;
-  uint32_t ca = 0u, cc = 0u;
+  ca = 0u;
+  cc = 0u;
   if (vec) {
     uint32_t ca_lane = 0u;   // keys above the window, this lane's share
+    uint32_t ccl = 0u;
     stream_segment4(row, s0, s1, [&](int L, const uint32_t (&x)[4], int nv) {
       uint32_t nc = 0u;
 #pragma unroll
@@ -426,7 +326,7 @@ __global__ __launch_bounds__(kStreamThreads) void topk_stream_kernel(const float
         nc += (j < nv && x[j] >= lo) ? 1u : 0u;
       }
       uint32_t tot;
-      uint32_t slot = cc + lane_prefix8(nc, tot);
+      uint32_t slot = ccl + lane_prefix8(nc, tot);
       if (tot != 0u) {   // wave-uniform
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -439,70 +339,42 @@ __global__ __launch_bounds__(kStreamThreads) void topk_stream_kernel(const float
           }
         }
       }
-      cc += tot;
+      ccl += tot;
     });
     ca = wave_sum_u32(ca_lane);
+    cc = ccl;
   } else {
+    uint32_t cal = 0u, ccl = 0u;
     stream_segment(row, s0, s1, [&](int L, uint32_t x, bool valid) {
-      ca += (uint32_t)__popcll(ballot(valid && x > hi));
+      cal += (uint32_t)__popcll(ballot(valid && x > hi));
       const bool c = valid && x >= lo;
       const uint64_t bm = ballot(c);
-      const uint32_t slot = cc + (uint32_t)lanes_below(bm);
+      const uint32_t slot = ccl + (uint32_t)lanes_below(bm);
       if (c && slot < (uint32_t)kCandPerWave) {
         sh.cand_key[cb + slot] = x;
         sh.cand_pos[cb + slot] = L;
       }
-      cc += (uint32_t)__popcll(bm);
+      ccl += (uint32_t)__popcll(bm);
     });
+    ca = cal;
+    cc = ccl;
   }
-  __syncthreads();   // bcast and red are free again
-  if (lane == 0) {
-    sh.red[w] = ca;
-    sh.red[kStreamWaves + w] = cc;
-  }
-  __syncthreads();
-  uint32_t c_above = 0u, c_cand = 0u, ccs[kStreamWaves];
-  bool fits = true;
-#pragma unroll
-  for (int i = 0; i < kStreamWaves; ++i) {
-    ccs[i] = sh.red[kStreamWaves + i];
-    c_above += sh.red[i];
-    c_cand += ccs[i];
-    fits = fits && ccs[i] <= (uint32_t)kCandPerWave;
-  }
-  const bool window_ok = fits && c_above < (uint32_t)k && (uint32_t)k <= c_cand;
+}
 
-  uint32_t T, need_eq, cnt_eq, gt_w, eq_w;
-  if (window_ok) {
-    lds_threshold(sh, ccs, hi, (uint32_t)k - c_above, T, need_eq, cnt_eq);
-    uint32_t g = 0u, e = 0u;
-    for (uint32_t b0 = 0; b0 < cc; b0 += kWave) {   // uniform bounds: every lane takes part in the ballots
-      const uint32_t i = b0 + (uint32_t)lane;
-      const bool in = i < cc;
-      const uint32_t x = in ? sh.cand_key[cb + i] : 0u;
-      g += (uint32_t)__popcll(ballot(in && x > T));
-      e += (uint32_t)__popcll(ballot(in && x == T));
-    }
-    gt_w = g;
-    eq_w = e;
-  } else {
-    stream_threshold(row, n, k, sh, T, need_eq, cnt_eq);
-    uint32_t g = 0u, e = 0u;
-    stream_segment(row, s0, s1, [&](int, uint32_t x, bool valid) {
-      g += (uint32_t)__popcll(ballot(valid && x > T));
-      e += (uint32_t)__popcll(ballot(valid && x == T));
-    });
-    gt_w = g;
-    eq_w = e;
-  }
-  // ---- output slots: T-valued keys are taken lowest positions first, i.e. by wave order, then in order
+// Output slots of the kept keys: keys > T, and the first need_eq T-valued keys in position order (wave order,
+// then in order within a wave). gt_w / eq_w: this wave's counts. Gives the wave's first slot and how many of its
+// T-valued keys it takes. Starts with a barrier (red is reused).
+__device__ __forceinline__ void stream_out_base(uint32_t gt_w, uint32_t eq_w, uint32_t need_eq, StreamShared &sh,
+                                                uint32_t &base, uint32_t &quota) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   __syncthreads();
   if (lane == 0) {
     sh.red[w] = gt_w;
     sh.red[kStreamWaves + w] = eq_w;
   }
   __syncthreads();
-  uint32_t eq_before = 0u, base = 0u;
+  uint32_t eq_before = 0u;
+  base = 0u;
 #pragma unroll
   for (int i = 0; i < kStreamWaves; ++i) {
     if (i < w) {
@@ -512,9 +384,16 @@ __global__ __launch_bounds__(kStreamThreads) void topk_stream_kernel(const float
       eq_before += ei;
     }
   }
-  const uint32_t quota = min(eq_w, need_eq > eq_before ? need_eq - eq_before : 0u);   // T-valued keys this wave takes
-  uint32_t eq_run = 0u;
-  auto put = [&](int L, uint32_t x, bool valid) {
+  quota = min(eq_w, need_eq > eq_before ? need_eq - eq_before : 0u);
+}
+
+// The ordered output walk: put(L, key, valid) is called in position order for this wave's elements;
+// emit(slot, L, key) for every kept one (slot < limit).
+template <class Emit>
+struct StreamPut {
+  uint32_t T, quota, base, eq_run, limit;
+  Emit emit;
+  __device__ __forceinline__ void operator()(int L, uint32_t x, bool valid) {
     const bool eq = valid && x == T;
     const uint64_t em = ballot(eq);
     const bool take = (valid && x > T) || (eq && eq_run + (uint32_t)lanes_below(em) < quota);
@@ -522,18 +401,193 @@ __global__ __launch_bounds__(kStreamThreads) void topk_stream_kernel(const float
     const uint64_t sm = ballot(take);
     if (take) {
       const uint32_t slot = base + (uint32_t)lanes_below(sm);
-      if (slot < (uint32_t)k) out[slot] = L;   // exactly k are taken; the guard only bounds the writes
+      if (slot < limit) emit(slot, L, x);   // exactly `limit` are taken; the guard only bounds the writes
     }
     base += (uint32_t)__popcll(sm);
-  };
-  if (window_ok) {
-    for (uint32_t b0 = 0; b0 < cc; b0 += kWave) {   // the wave's candidates, in position order
-      const uint32_t i = b0 + (uint32_t)lane;
-      const bool in = i < cc;
-      put(in ? sh.cand_pos[cb + i] : 0, in ? sh.cand_key[cb + i] : 0u, in);
+  }
+};
+
+// Emit the kept keys of this wave's row segment [s0, s1), read again from the scores.
+template <class Emit>
+__device__ __forceinline__ void stream_emit_row(const float *__restrict__ row, int s0, int s1, uint32_t T,
+                                                uint32_t need_eq, uint32_t limit, StreamShared &sh, Emit emit) {
+  uint32_t g = 0u, e = 0u;
+  stream_segment(row, s0, s1, [&](int, uint32_t x, bool valid) {
+    g += (uint32_t)__popcll(ballot(valid && x > T));
+    e += (uint32_t)__popcll(ballot(valid && x == T));
+  });
+  uint32_t base, quota;
+  stream_out_base(g, e, need_eq, sh, base, quota);
+  StreamPut<Emit> put{T, quota, base, 0u, limit, emit};
+  stream_segment(row, s0, s1, [&](int L, uint32_t x, bool valid) { put(L, x, valid); });
+}
+
+// Selection among the candidates of the four wave LDS regions (wave v's region holds ccs[v] <= kCandPerWave
+// (key, position) pairs in position order): the `need` largest of the keys <= top are kept, together with every
+// candidate above top; emit(slot, position, key) for each kept one (slot < limit), in position order (wave order,
+// then region order). Each lane loads its region entries j = u * 64 + lane into registers once, so the bucket
+// passes count from registers, with no LDS reads between them. The passes stop as soon as the bin holding the
+// need-th key is to be kept whole: then every key >= the bin's lower bound is kept (T = that bound, all T-valued).
+constexpr int kRegItems = (kCandPerWave + kWave - 1) / kWave;   // 16
+// With `rank_above` set, `need` counts the candidates above top too (need = k): they are counted here, and if
+// they are k or more the search runs over every candidate instead.
+template <class Emit>
+__device__ __forceinline__ void regions_select_emit(const uint32_t (&ccs)[kStreamWaves], uint32_t top, uint32_t need,
+                                                    uint32_t limit, StreamShared &sh, Emit emit,
+                                                    bool rank_above = false) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int cb = w * kCandPerWave;
+  const uint32_t cnt = ccs[w];
+  uint32_t key[kRegItems];
+  int32_t pos[kRegItems];
+#pragma unroll
+  for (int u = 0; u < kRegItems; ++u) {
+    const uint32_t j = (uint32_t)(u * kWave + lane);
+    key[u] = j < cnt ? sh.cand_key[cb + j] : 0u;
+    pos[u] = j < cnt ? sh.cand_pos[cb + j] : 0;
+  }
+  if (rank_above) {
+    uint32_t a = 0u;
+#pragma unroll
+    for (int u = 0; u < kRegItems; ++u) a += (uint32_t)__popcll(ballot((uint32_t)(u * kWave + lane) < cnt && key[u] > top));
+    __syncthreads();   // red is free
+    if (lane == 0) sh.red[w] = a;
+    __syncthreads();
+    uint32_t above = 0u;
+#pragma unroll
+    for (int i = 0; i < kStreamWaves; ++i) above += sh.red[i];
+    if (above >= need) top = 0xffffffffu;   // the need-th key lies above the window: search every candidate
+    else need -= above;
+  }
+  auto in_win = [&](int u) { return (uint32_t)(u * kWave + lane) < cnt && key[u] <= top; };
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int u = 0; u < kRegItems; ++u) {
+    if (in_win(u)) {
+      kmin = min(kmin, key[u]);
+      kmax = max(kmax, key[u]);
     }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  }
+  __syncthreads();   // red and bcast are free
+  if (lane == 0) {
+    sh.red[w] = kmin;
+    sh.red[kStreamWaves + w] = kmax;
+  }
+  __syncthreads();
+  kmin = sh.red[0];
+  kmax = sh.red[kStreamWaves];
+#pragma unroll
+  for (int i = 1; i < kStreamWaves; ++i) {
+    kmin = min(kmin, sh.red[i]);
+    kmax = max(kmax, sh.red[kStreamWaves + i]);
+  }
+  uint32_t lo = kmin, hi = kmax, T, need_eq;
+  const uint32_t range = kmax - kmin;
+  int shift = range == 0u ? 0 : max(0, 32 - __clz((int)range) - kBinBits);
+  while (true) {
+    __syncthreads();
+    stream_clear_hist(sh);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kRegItems; ++u)
+      if (in_win(u) && key[u] >= lo && key[u] <= hi) atomicAdd(&sh.hist[(key[u] - lo) >> shift], 1u);
+    __syncthreads();
+    const int rr[1] = {(int)need};
+    stream_rank_bins<1>(sh, rr);
+    const uint32_t B = sh.bcast[0], above = sh.bcast[1], inbin = sh.bcast[2];
+    need -= above;
+    lo += B << shift;
+    hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + ((1ull << shift) - 1ull));
+    if (shift == 0 || inbin == need) {   // every key of the bin is kept: it is enough to keep all keys >= lo
+      T = lo;
+      need_eq = shift == 0 ? need : 0xffffffffu;
+      break;
+    }
+    shift = max(0, shift - kBinBits);
+  }
+  uint32_t g = 0u, e = 0u;
+#pragma unroll
+  for (int u = 0; u < kRegItems; ++u) {
+    const bool in = (uint32_t)(u * kWave + lane) < cnt;
+    g += (uint32_t)__popcll(ballot(in && key[u] > T));
+    e += (uint32_t)__popcll(ballot(in && key[u] == T));
+  }
+  uint32_t base, quota;
+  stream_out_base(g, e, need_eq, sh, base, quota);
+  StreamPut<Emit> put{T, quota, base, 0u, limit, emit};
+#pragma unroll
+  for (int u = 0; u < kRegItems; ++u) {
+    const bool in = (uint32_t)(u * kWave + lane) < cnt;
+    put(pos[u], key[u], in);
+  }
+}
+
+// Per-wave counts after stream_collect: the totals, and whether every wave's keys fit its region.
+__device__ __forceinline__ void stream_counts(uint32_t ca, uint32_t cc, StreamShared &sh, uint32_t (&ccs)[kStreamWaves],
+                                              uint32_t &c_above, uint32_t &c_cand, bool &fits) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  __syncthreads();   // bcast and red are free again
+  if (lane == 0) {
+    sh.red[w] = ca;
+    sh.red[kStreamWaves + w] = cc;
+  }
+  __syncthreads();
+  c_above = 0u;
+  c_cand = 0u;
+  fits = true;
+#pragma unroll
+  for (int i = 0; i < kStreamWaves; ++i) {
+    ccs[i] = sh.red[kStreamWaves + i];
+    c_above += sh.red[i];
+    c_cand += ccs[i];
+    fits = fits && ccs[i] <= (uint32_t)kCandPerWave;
+  }
+}
+
+// Segments of the 4 waves over [0, n): starts at multiples of 256 positions (16-byte aligned when the row is).
+__device__ __forceinline__ void stream_segment_of(int n, int &s0, int &s1) {
+  const int w = threadIdx.x / kWave;
+  const int seg = ((n + kStreamWaves - 1) / kStreamWaves + 4 * kWave - 1) / (4 * kWave) * (4 * kWave);
+  s0 = min(n, w * seg);
+  s1 = min(n, s0 + seg);
+}
+
+__global__ __launch_bounds__(kStreamThreads) void topk_stream_kernel(const float *__restrict__ scores, int64_t ld,
+                                                                     const int32_t *__restrict__ q_pos, int num_q,
+                                                                     int k, int32_t *__restrict__ idx) {
+  __shared__ StreamShared sh;
+  const int r = num_q - 1 - (int)blockIdx.x;    // longest rows of a prefill first
+  const int n = q_pos[r] + 1;
+  int32_t *out = idx + (int64_t)r * k;
+  const int tid = threadIdx.x;
+  if (n <= k) {
+    for (int j = tid; j < k; j += kStreamThreads) out[j] = j < n ? j : -1;
+    return;
+  }
+  const float *row = scores + (int64_t)r * ld;
+  const bool vec = (ld & 3) == 0 && ((uintptr_t)scores & 15) == 0;
+  int s0, s1;
+  stream_segment_of(n, s0, s1);
+  uint32_t lo, hi;
+  stream_window(row, n, k, sh, lo, hi);
+  uint32_t ca, cc;
+  stream_collect(row, s0, s1, vec, lo, hi, sh, ca, cc);
+  uint32_t ccs[kStreamWaves], c_above, c_cand;
+  bool fits;
+  stream_counts(ca, cc, sh, ccs, c_above, c_cand, fits);
+  const bool window_ok = fits && c_above < (uint32_t)k && (uint32_t)k <= c_cand;
+  auto emit = [&](uint32_t slot, int L, uint32_t) { out[slot] = L; };
+  if (window_ok) {
+    regions_select_emit(ccs, hi, (uint32_t)k - c_above, (uint32_t)k, sh, emit);
   } else {
-    stream_segment(row, s0, s1, put);
+    uint32_t T, need_eq, cnt_eq;
+    stream_threshold(row, n, k, sh, T, need_eq, cnt_eq);
+    stream_emit_row(row, s0, s1, T, need_eq, (uint32_t)k, sh, emit);
   }
 }
 
@@ -564,16 +618,223 @@ hipError_t launch_topk_rows(const float *scores, int64_t ld, const int32_t *q_po
   }
 }
 
-template <int IA, int IB>
-static hipError_t launch_chunked_t(const float *scores, int64_t ld, const int32_t *q_pos, int num_q, int k,
-                                   int chunk, int n_chunks, uint32_t *ck, int32_t *cp, int32_t *idx,
-                                   hipStream_t s) {
-  hipLaunchKernelGGL(topk_chunk_kernel<IA>, dim3(num_q, n_chunks), dim3(kTopkBlock), 0, s, scores, ld, q_pos, k,
-                     chunk, n_chunks, ck, cp);
+// ---------------------------------------------------------------------------------------------------------
+// Windowed chunked form for batches of few rows (decode): each row is split into chunks of `chunk` keys, one
+// 256-thread workgroup per chunk, so the batch fills the chip. Every workgroup of a row takes the same sample of
+// the row as the streaming form (the runs are read from L2 after the first workgroup) and derives the same lower
+// bound lo of the window that holds the k-th best key. Chunk c keeps its keys >= lo in LDS during one pass (the
+// streaming form's collect step over its four wave segments) and writes them, in position order, with their
+// count: a few hundred per chunk instead of k. A chunk with more than cap = min(k, chunk) such keys, or more than
+// a wave's LDS region holds, writes its own exact top-cap instead (it contains the row's top-k within that chunk
+// under the same total order). The merge pass (one workgroup per row) gathers the row's M candidates into LDS, in
+// position order, and selects k among them with the streaming form's LDS search. When M >= k the selection is
+// exact (the k-th best key is then >= lo, so every kept key is a candidate); when M < k the window missed and
+// the merge selects over the whole row from the scores instead (as does a row with too many candidates for LDS).
+constexpr int kWMaxChunks = kStreamThreads;   // one count per merge thread
+constexpr int kWMergeCap = kStreamWaves * kCandPerWave;
+
+// Pass 1: chunk c of row r writes its candidates at slot (r * n_chunks + c) * cap and their count at
+// cnt[r * n_chunks + c]; chunk 0 also writes the window's top at cnt[num_q * n_chunks + r]. The chunk (V * 1024 keys) is loaded into registers before the window is known: wave w
+// holds positions w*V*256 .. (w+1)*V*256 - 1, lane l four consecutive positions per load, so lane order within a
+// load is position order.
+template <int V>
+__global__ __launch_bounds__(kStreamThreads) void topk_wchunk_kernel(const float *__restrict__ scores, int64_t ld,
+                                                                     const int32_t *__restrict__ q_pos, int k,
+                                                                     int n_chunks, int cap,
+                                                                     uint32_t *__restrict__ cand_key,
+                                                                     int32_t *__restrict__ cand_pos,
+                                                                     uint32_t *__restrict__ cand_cnt) {
+  constexpr int CHUNK = V * 4 * kStreamThreads;
+  __shared__ StreamShared sh;
+  const int r = blockIdx.x, c = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int start = c * CHUNK;
+  const float *row = scores + (int64_t)r * ld;
+  const float *crow = row + start;
+  // keys of the chunk within the row's allocation (ld), loaded with q_pos; masked to the row's length below
+  const int avail = (int)min((int64_t)CHUNK, ld - start);
+  const bool vec = (ld & 3) == 0 && ((uintptr_t)scores & 15) == 0;
+  const int wbase = w * V * 4 * kWave;
+  f32x4 x[V];
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const int L = wbase + u * 4 * kWave + 4 * lane;
+    if (vec && L + 3 < avail) {
+      x[u] = *(const f32x4 *)(crow + L);
+    } else {
+      x[u].x = L + 0 < avail ? crow[L + 0] : 0.f;
+      x[u].y = L + 1 < avail ? crow[L + 1] : 0.f;
+      x[u].z = L + 2 < avail ? crow[L + 2] : 0.f;
+      x[u].w = L + 3 < avail ? crow[L + 3] : 0.f;
+    }
+  }
+  const int n = q_pos[r] + 1;
+  if (n <= k || start >= n) return;   // the merge pass writes rows with n <= k directly
+  const int len = min(CHUNK, n - start);
+  uint32_t lo, hi;
+  stream_window(row, n, k, sh, lo, hi);
+  // keys >= lo of this wave's positions -> its LDS region, in position order
+  const int cb = w * kCandPerWave;
+  uint32_t cc = 0u;
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const int L = wbase + u * 4 * kWave + 4 * lane;
+    const uint32_t kx[4] = {order_key(x[u].x), order_key(x[u].y), order_key(x[u].z), order_key(x[u].w)};
+    uint32_t nc = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nc += (L + j < len && kx[j] >= lo) ? 1u : 0u;
+    uint32_t tot;
+    uint32_t slot = cc + lane_prefix8(nc, tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (L + j < len && kx[j] >= lo) {
+        if (slot < (uint32_t)kCandPerWave) {
+          sh.cand_key[cb + slot] = kx[j];
+          sh.cand_pos[cb + slot] = L + j;
+        }
+        ++slot;
+      }
+    }
+    cc += tot;
+  }
+  uint32_t ccs[kStreamWaves], c_above, c_cand;
+  bool fits;
+  stream_counts(0u, cc, sh, ccs, c_above, c_cand, fits);
+  const int64_t dst = ((int64_t)r * n_chunks + c) * cap;
+  if (fits && c_cand <= (uint32_t)cap) {
+    uint32_t base = 0u;
+#pragma unroll
+    for (int i = 0; i < kStreamWaves; ++i) base += i < w ? ccs[i] : 0u;
+    for (uint32_t i = lane; i < cc; i += kWave) {
+      cand_key[dst + base + i] = sh.cand_key[cb + i];
+      cand_pos[dst + base + i] = start + sh.cand_pos[cb + i];
+    }
+  } else {   // the chunk's own exact top-cap, by streaming bucket passes over its scores (rare)
+    int s0, s1;
+    stream_segment_of(len, s0, s1);
+    uint32_t T, need_eq, cnt_eq;
+    stream_threshold(crow, len, cap, sh, T, need_eq, cnt_eq);
+    stream_emit_row(crow, s0, s1, T, need_eq, (uint32_t)cap, sh, [&](uint32_t slot, int L, uint32_t xk) {
+      cand_key[dst + slot] = xk;
+      cand_pos[dst + slot] = start + L;
+    });
+    c_cand = (uint32_t)cap;
+  }
+  if (tid == 0) {
+    cand_cnt[(int64_t)r * n_chunks + c] = c_cand;
+    if (c == 0) cand_cnt[(int64_t)gridDim.x * n_chunks + r] = hi;   // the window's top, for the merge
+  }
+}
+
+// Pass 2: one workgroup per row selects k among its M candidates (or, when M < k or M exceeds the LDS regions,
+// over the whole row).
+__global__ __launch_bounds__(kStreamThreads) void topk_wmerge_kernel(const float *__restrict__ scores, int64_t ld,
+                                                                     const int32_t *__restrict__ q_pos, int k,
+                                                                     int chunk, int n_chunks, int cap,
+                                                                     const uint32_t *__restrict__ cand_key,
+                                                                     const int32_t *__restrict__ cand_pos,
+                                                                     const uint32_t *__restrict__ cand_cnt,
+                                                                     int32_t *__restrict__ idx) {
+  __shared__ StreamShared sh;
+  __shared__ uint32_t pre[kWMaxChunks + 1];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  // the counts are loaded with q_pos (chunks past the row's end are masked once n is known)
+  const uint32_t v_raw = tid < n_chunks ? cand_cnt[(int64_t)r * n_chunks + tid] : 0u;
+  const int n = q_pos[r] + 1;
+  int32_t *out = idx + (int64_t)r * k;
+  if (n <= k) {
+    for (int j = tid; j < k; j += kStreamThreads) out[j] = j < n ? j : -1;
+    return;
+  }
+  const int used = (n + chunk - 1) / chunk;   // <= n_chunks <= kWMaxChunks
+  const uint32_t v = tid < used ? v_raw : 0u;
+  const uint32_t incl = stream_incl_scan(v, sh);
+  if (tid < used) pre[tid + 1] = incl;
+  if (tid == 0) pre[0] = 0u;
+  __syncthreads();
+  const uint32_t M = pre[used];
+  const float *row = scores + (int64_t)r * ld;
+  auto emit = [&](uint32_t slot, int L, uint32_t) { out[slot] = L; };
+  if (M < (uint32_t)k || M > (uint32_t)kWMergeCap) {
+    int s0, s1;
+    stream_segment_of(n, s0, s1);
+    uint32_t T, need_eq, cnt_eq;
+    stream_threshold(row, n, k, sh, T, need_eq, cnt_eq);
+    stream_emit_row(row, s0, s1, T, need_eq, (uint32_t)k, sh, emit);
+    return;
+  }
+  // candidates -> LDS, flat in position order (chunk order, then order within the chunk); every load is issued
+  // before the first store, so the row pays one memory latency
+  const int64_t base = (int64_t)r * n_chunks * cap;
+  constexpr int PM = (kWMergeCap + kStreamThreads - 1) / kStreamThreads;
+  uint32_t mk[PM];
+  int32_t mp[PM];
+#pragma unroll
+  for (int u = 0; u < PM; ++u) {
+    const uint32_t j = (uint32_t)(u * kStreamThreads + tid);
+    mk[u] = 0u;
+    mp[u] = 0;
+    if (j < M) {
+      int a = 0, b = used;   // chunk of flat entry j: pre[a] <= j < pre[a + 1]
+      while (b - a > 1) {
+        const int mid = (a + b) >> 1;
+        if (pre[mid] <= j) a = mid; else b = mid;
+      }
+      const int64_t g = base + (int64_t)a * cap + (j - pre[a]);
+      mk[u] = cand_key[g];
+      mp[u] = cand_pos[g];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PM; ++u) {
+    const uint32_t j = (uint32_t)(u * kStreamThreads + tid);
+    if (j < M) {
+      sh.cand_key[j] = mk[u];
+      sh.cand_pos[j] = mp[u];
+    }
+  }
+  __syncthreads();
+  // the flat array seen as the four wave regions of the streaming form
+  uint32_t ccs[kStreamWaves];
+#pragma unroll
+  for (int i = 0; i < kStreamWaves; ++i)
+    ccs[i] = (uint32_t)min(max((int)M - i * kCandPerWave, 0), kCandPerWave);
+  (void)lane;
+  (void)w;
+  const uint32_t top = cand_cnt[(int64_t)gridDim.x * n_chunks + r];   // written by chunk 0 of this row
+  regions_select_emit(ccs, top, (uint32_t)k, (uint32_t)k, sh, emit, true);
+}
+
+size_t topk_windowed_ws_bytes(int num_q, int n_chunks, int cap) {
+  const size_t pairs = (size_t)num_q * n_chunks * cap;
+  return (pairs * 8 + 15) / 16 * 16 + (size_t)num_q * (n_chunks + 1) * 4;   // + counts, + each row's window top
+}
+
+template <int V>
+static void launch_wchunk(const float *scores, int64_t ld, const int32_t *q_pos, int num_q, int k, int n_chunks, int cap,
+                          uint32_t *ck, int32_t *cp, uint32_t *cc, hipStream_t s) {
+  hipLaunchKernelGGL(topk_wchunk_kernel<V>, dim3(num_q, n_chunks), dim3(kStreamThreads), 0, s, scores, ld, q_pos, k,
+                     n_chunks, cap, ck, cp, cc);
+}
+
+hipError_t launch_topk_windowed(const float *scores, int64_t ld, const int32_t *q_pos, int num_q, int k, int chunk,
+                                int n_chunks, void *ws, int32_t *idx, hipStream_t s) {
+  if (n_chunks > kWMaxChunks) return hipErrorInvalidValue;
+  const int cap = min(k, chunk);
+  const size_t pairs = (size_t)num_q * n_chunks * cap;
+  uint32_t *ck = static_cast<uint32_t *>(ws);
+  int32_t *cp = reinterpret_cast<int32_t *>(ck + pairs);
+  uint32_t *cc = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) + (pairs * 8 + 15) / 16 * 16);
+  switch (chunk) {
+    case 4096: launch_wchunk<4>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
+    case 8192: launch_wchunk<8>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
+    case 16384: launch_wchunk<16>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_merge_kernel<IB>, dim3(num_q), dim3(kTopkBlock), 0, s, q_pos, k, chunk, n_chunks, ck, cp,
-                     idx);
+  hipLaunchKernelGGL(topk_wmerge_kernel, dim3(num_q), dim3(kStreamThreads), 0, s, scores, ld, q_pos, k, chunk,
+                     n_chunks, cap, ck, cp, cc, idx);
   return hipGetLastError();
 }
 
@@ -590,35 +851,6 @@ hipError_t launch_topk_merge(const int32_t *q_pos, int num_q, int k, int chunk, 
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
-}
-
-template <int IA>
-static hipError_t launch_chunked_a(const float *scores, int64_t ld, const int32_t *q_pos, int num_q, int k,
-                                   int chunk, int n_chunks, uint32_t *ck, int32_t *cp, int32_t *idx,
-                                   int items_b, hipStream_t s) {
-  switch (items_b) {
-    case 1: return launch_chunked_t<IA, 1>(scores, ld, q_pos, num_q, k, chunk, n_chunks, ck, cp, idx, s);
-    case 2: return launch_chunked_t<IA, 2>(scores, ld, q_pos, num_q, k, chunk, n_chunks, ck, cp, idx, s);
-    case 4: return launch_chunked_t<IA, 4>(scores, ld, q_pos, num_q, k, chunk, n_chunks, ck, cp, idx, s);
-    case 8: return launch_chunked_t<IA, 8>(scores, ld, q_pos, num_q, k, chunk, n_chunks, ck, cp, idx, s);
-    case 16: return launch_chunked_t<IA, 16>(scores, ld, q_pos, num_q, k, chunk, n_chunks, ck, cp, idx, s);
-    case 32: return launch_chunked_t<IA, 32>(scores, ld, q_pos, num_q, k, chunk, n_chunks, ck, cp, idx, s);
-    case 64: return launch_chunked_t<IA, 64>(scores, ld, q_pos, num_q, k, chunk, n_chunks, ck, cp, idx, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_topk_chunked(const float *scores, int64_t ld, const int32_t *q_pos, int num_q, int k, int chunk,
-                               int n_chunks, uint32_t *cand_key, int32_t *cand_pos, int32_t *idx, int items_a,
-                               int items_b, hipStream_t s) {
-  switch (items_a) {
-    case 4: return launch_chunked_a<4>(scores, ld, q_pos, num_q, k, chunk, n_chunks, cand_key, cand_pos, idx, items_b, s);
-    case 8: return launch_chunked_a<8>(scores, ld, q_pos, num_q, k, chunk, n_chunks, cand_key, cand_pos, idx, items_b, s);
-    case 16: return launch_chunked_a<16>(scores, ld, q_pos, num_q, k, chunk, n_chunks, cand_key, cand_pos, idx, items_b, s);
-    case 32: return launch_chunked_a<32>(scores, ld, q_pos, num_q, k, chunk, n_chunks, cand_key, cand_pos, idx, items_b, s);
-    case 64: return launch_chunked_a<64>(scores, ld, q_pos, num_q, k, chunk, n_chunks, cand_key, cand_pos, idx, items_b, s);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 }  // namespace dsa
