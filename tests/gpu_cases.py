@@ -53,7 +53,10 @@ def indexer_rel_err(got, ref, fp8=False):
     tol = 5e-2 if fp8 else 1e-2
     floor = 1e-3 * max(float(np.abs(ref).max()), 1e-30)
     bound = tol * np.maximum(np.abs(ref), floor)
-    return float((np.abs(got.astype(np.float64) - ref) / bound).max())
+    err = np.abs(got.astype(np.float64) - ref) / bound
+    if not np.isfinite(err).all():   # an unwritten (NaN-filled) or non-finite score fails outright
+        return float("inf")
+    return float(err.max())
 
 
 def run_indexer(wl_dev, b, fill=float("nan")):
