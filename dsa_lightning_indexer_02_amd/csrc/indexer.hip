@@ -183,11 +183,12 @@ __global__ __launch_bounds__(NW * kWave) void indexer_kernel(IndexerArgs a, int 
   }
 }
 
-// Contiguous key caches: the same product, with the key tiles streamed into LDS by a dedicated producer
-// wave. Wave NW issues every 16-byte global->LDS load of a tile (three tiles in flight) and is the only wave
-// that waits on vector-memory counts, so the compute waves' score stores never delay a tile. Rows keep their
-// natural 1 KB-contiguous layout in LDS with the 16-byte chunks of key row kk XOR-swizzled by kk, which keeps
-// the MFMA operand reads free of bank conflicts without padding.
+// The same product with the key tiles streamed into LDS by a dedicated producer wave. Wave NW issues every
+// 16-byte global->LDS load of a tile (three tiles in flight) and is the only wave that waits on vector-memory
+// counts, so the compute waves' score stores never delay a tile. Rows keep their natural 1 KB-contiguous layout
+// in LDS with the 16-byte chunks of key row kk XOR-swizzled by kk, which keeps the MFMA operand reads free of
+// bank conflicts without padding. Paged caches (pages of at least RPL rows) take the same loads: the rows of one
+// load lie in one page, whose id the producer reads with a scalar load and keeps in LDS for the scale lookups.
 template <int HI, int DI, bool FP8, int ROWS, int NW>
 struct PipeCfg {
   using B = IndexerCfg<HI, DI, FP8, ROWS, NW>;
@@ -201,18 +202,82 @@ struct PipeCfg {
   __device__ static __forceinline__ int swz(int chunk, int kk) { return chunk ^ (kk & (B::CPK - 1)); }
 };
 
-template <int HI, int DI, bool FP8, int ROWS, int NW>
+// Balanced split of a batch of few rows per sequence (decode): the key blocks of every row block (row block rb
+// has p_max(rb) / BK + 1 of them, p_max the largest position of its rows) are cut into chunks of
+// bpc = ceil(total / target) blocks, ceil(nb / bpc) chunks per row block, and workgroup u takes the u-th chunk in
+// row-block order, so a long sequence gets proportionally more workgroups than a short one. Every wave computes
+// the same split from q_pos; false for a workgroup past the last chunk.
+template <int ROWS, int BK>
+__device__ __forceinline__ bool balanced_unit(const IndexerArgs &a, int row_blocks, int target, int u, int &rb,
+                                              int &c, int &bpc) {
+  const int lane = threadIdx.x & 63;
+  auto nblocks = [&](int r) {
+    int p = -1;
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+      const int row = r * ROWS + i;
+      if (row < a.num_q) p = max(p, a.q_pos[row]);
+    }
+    return p < 0 ? 0 : p / BK + 1;
+  };
+  auto wave_sum = [](int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+  };
+  int total = 0;
+  for (int base = 0; base < row_blocks; base += kWave) {
+    const int r = base + lane;
+    total += wave_sum(r < row_blocks ? nblocks(r) : 0);
+  }
+  bpc = max(1, (total + target - 1) / target);
+  int before = 0;
+  for (int base = 0; base < row_blocks; base += kWave) {
+    const int r = base + lane;
+    const int ch = r < row_blocks ? (nblocks(r) + bpc - 1) / bpc : 0;
+    int incl = ch;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    const uint64_t m = ballot(ch > 0 && u >= before + incl - ch && u < before + incl);
+    if (m != 0) {
+      const int src = __ffsll((unsigned long long)m) - 1;
+      rb = __shfl(r, src);
+      c = u - (before + __shfl(incl - ch, src));
+      return true;
+    }
+    before += __shfl(incl, kWave - 1);
+  }
+  return false;
+}
+
+template <int HI, int DI, bool FP8, int ROWS, int NW, bool PAGED>
 __global__ __launch_bounds__((NW + 1) * kWave) void indexer_pipe_kernel(IndexerArgs a, int blocks_per_chunk,
-                                                                         int row_blocks) {
+                                                                         int row_blocks, int balance_target) {
   using C = IndexerCfg<HI, DI, FP8, ROWS, NW>;
   using P = PipeCfg<HI, DI, FP8, ROWS, NW>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[P::NBUF * P::TILE];
+  __shared__ int32_t lds_page[P::NBUF][P::LOADS];   // paged caches: the page of each load of a tile
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool producer = wv == NW;
   const int n = lane & 31, g = lane >> 5;
-  const int rb = row_blocks - 1 - (int)blockIdx.x;   // heavy row blocks (late positions, most keys) first
+  int rb, kb_base, bpc;
+  if (balance_target > 0) {
+    int c;
+    if (!balanced_unit<ROWS, C::BK>(a, row_blocks, balance_target, (int)blockIdx.x, rb, c, bpc)) return;
+    rb = __builtin_amdgcn_readfirstlane(rb);   // wave-uniform values: keep them (and the addresses) scalar
+    c = __builtin_amdgcn_readfirstlane(c);
+    bpc = __builtin_amdgcn_readfirstlane(bpc);
+    kb_base = c * bpc;
+  } else {
+    rb = row_blocks - 1 - (int)blockIdx.x;   // heavy row blocks (late positions, most keys) first
+    bpc = blocks_per_chunk;
+    kb_base = (int)blockIdx.y * bpc;
+  }
   const int r0 = rb * ROWS;
   const int my_slot = wv % ROWS;
   const int my_part = wv / ROWS;
@@ -220,6 +285,8 @@ __global__ __launch_bounds__((NW + 1) * kWave) void indexer_pipe_kernel(IndexerA
   const bool row_ok = !producer && my_row < a.num_q;
   const int my_p = row_ok ? a.q_pos[my_row] : -1;
   const int my_seq = row_ok ? a.q_seq[my_row] : -1;
+  constexpr bool paged = PAGED;
+  const int shift = a.slot.page_shift;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds_k;
   const int q_ld = lane / C::CPK;   // producer lanes: key row within a load, and the NV chunk offsets
   int coff[P::NV];
@@ -256,18 +323,35 @@ __global__ __launch_bounds__((NW + 1) * kWave) void indexer_pipe_kernel(IndexerA
       ++seg_end;
     }
     const bool active = row_ok && my_seq == b && my_slot >= seg && my_slot < seg_end;
-    const int kb_lo = blockIdx.y * blocks_per_chunk;
-    const int kb_hi = min(kb_lo + blocks_per_chunk, p_max / C::BK + 1);
-    const uint8_t *kseq = (const uint8_t *)a.k_idx + (int64_t)b * a.slot.seq_stride * C::ROW_BYTES;
+    const int kb_lo = kb_base;
+    const int kb_hi = min(kb_lo + bpc, p_max / C::BK + 1);
+    const uint8_t *kbase = (const uint8_t *)a.k_idx;
+    const int64_t seq0 = (int64_t)b * a.slot.seq_stride;   // contiguous: slot of position 0
+    const int32_t *ptab = paged ? a.slot.page_table + (int64_t)b * a.slot.max_pages : nullptr;
     // producer: tile kb into buffer kb % NBUF; keys past p_max load key p_max (never scored). Load j fills key
     // rows j*RPL .. j*RPL+RPL-1 of the tile; lane (q, pc) writes chunk pc of row j*RPL + q, fetching logical
-    // chunk swz(pc, row). The swizzle repeats every NV loads, so a lane needs only NV source offsets.
+    // chunk swz(pc, row). The swizzle repeats every NV loads, so a lane needs only NV source offsets. For a paged
+    // cache the page ids of all the tile's loads are read first (scalar loads, one wait), then the loads go out.
     auto issue = [&](int kb) {
-      const uint32_t dst = lds_base + (uint32_t)((kb % P::NBUF) * P::TILE);
+      const int buf = kb % P::NBUF;
+      const uint32_t dst = lds_base + (uint32_t)(buf * P::TILE);
+      int32_t pg[P::LOADS];
+      if constexpr (paged) {
+#pragma unroll
+        for (int j = 0; j < P::LOADS; ++j) pg[j] = ptab[min(kb * C::BK + j * P::RPL, p_max) >> shift];
+        if (lane == 0) {
+#pragma unroll
+          for (int j = 0; j < P::LOADS; ++j) lds_page[buf][j] = pg[j];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < P::LOADS; ++j) {
         const int s = min(kb * C::BK + j * P::RPL + q_ld, p_max);
-        const uint64_t src = (uint64_t)(kseq + (int64_t)s * C::ROW_BYTES + coff[j % P::NV]);
+        uint64_t src;
+        if constexpr (paged)
+          src = (uint64_t)(kbase + (((int64_t)pg[j] << shift) + (s & ((1 << shift) - 1))) * C::ROW_BYTES + coff[j % P::NV]);
+        else
+          src = (uint64_t)(kbase + (seq0 + s) * C::ROW_BYTES + coff[j % P::NV]);
         load_lds_16(src, dst + (uint32_t)(j * kWave * 16));
       }
     };
@@ -281,18 +365,25 @@ __global__ __launch_bounds__((NW + 1) * kWave) void indexer_pipe_kernel(IndexerA
           // tile kb has landed once at most tile kb+1's loads are outstanding (loads complete in order)
           if (kb + 1 < kb_hi) wait_vmcnt<(P::LOADS < 64 ? P::LOADS : 0)>(); else wait_vmcnt<0>();
         }
-        lds_barrier();  // tile kb visible to every wave; every wave is done with tile kb-1
+        lds_barrier();  // tile kb (and its page ids) visible to every wave; every wave is done with tile kb-1
         if (producer) {
           if (kb + 2 < kb_hi) issue(kb + 2);
         } else if (active) {
-          const uint8_t *tile = lds_k + (kb % P::NBUF) * P::TILE;
+          const int buf = kb % P::NBUF;
+          const uint8_t *tile = lds_k + buf * P::TILE;
 #pragma unroll 1
           for (int gi = 0; gi < C::GPW; ++gi) {   // one group's accumulators live at a time
             const int grp = my_part * C::GPW + gi;
             const int s0 = kb * C::BK + grp * 32;
             if (s0 > my_p) continue;  // wave-uniform: the whole group is beyond this row
             float sig = 1.f;
-            if constexpr (FP8) sig = a.k_scale[(int64_t)b * a.slot.seq_stride + min(s0 + n, my_p)];
+            if constexpr (FP8) {
+              const int sk = min(s0 + n, my_p);
+              if constexpr (paged)
+                sig = a.k_scale[((int64_t)lds_page[buf][(sk - kb * C::BK) / P::RPL] << shift) + (sk & ((1 << shift) - 1))];
+              else
+                sig = a.k_scale[seq0 + sk];
+            }
             f32x16 acc[C::MT];
 #pragma unroll
             for (int t = 0; t < C::MT; ++t) acc[t] = f32x16{};
@@ -752,9 +843,18 @@ static hipError_t launch_t(const IndexerArgs &a, int target_wgs, hipStream_t st)
   const Split sp = key_split(a.max_kv_len, C::BK, row_blocks, target_wgs);
   const int chunks = sp.chunks, bpc = sp.bpc;
   if constexpr (PipeCfg<HI, DI, FP8, ROWS, NW>::OK) {
-    if (a.slot.page_table == nullptr) {
-      hipLaunchKernelGGL((indexer_pipe_kernel<HI, DI, FP8, ROWS, NW>), dim3(row_blocks, chunks),
-                         dim3((NW + 1) * kWave), 0, st, a, bpc, row_blocks);
+    using P = PipeCfg<HI, DI, FP8, ROWS, NW>;
+    // paged caches whose pages hold whole loads (page_size >= RPL); fewer than 8 rows per workgroup (decode):
+    // the balanced split, about target_wgs workgroups in all
+    const bool paged = a.slot.page_table != nullptr;
+    if (!paged || (1 << a.slot.page_shift) >= P::RPL) {
+      auto kern = paged ? indexer_pipe_kernel<HI, DI, FP8, ROWS, NW, true> : indexer_pipe_kernel<HI, DI, FP8, ROWS, NW, false>;
+      if (ROWS < 8) {
+        hipLaunchKernelGGL(kern, dim3(target_wgs + row_blocks), dim3((NW + 1) * kWave), 0, st, a, 0, row_blocks,
+                           target_wgs);
+      } else {
+        hipLaunchKernelGGL(kern, dim3(row_blocks, chunks), dim3((NW + 1) * kWave), 0, st, a, bpc, row_blocks, 0);
+      }
       return hipGetLastError();
     }
   }
