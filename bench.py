@@ -579,7 +579,9 @@ def ingest_counters(d: str, workload: str, cmds: dict, stats):
            "Commands (from the repository root, R = its path; `cd /tmp && export TMPDIR=/tmp` first; one pass each):", ""]
     txt += [f"    {cmds[n].replace('DIR', d.rstrip('/'))}" for n in COUNTER_PASSES]
     txt += ["", "Derived here, per launch (counter values are summed over the chip by rocprofv3):",
-            f"- clock = GRBM_GUI_ACTIVE / {N_XCC} XCDs / the kernel-trace average duration;",
+            f"- clock = GRBM_GUI_ACTIVE / {N_XCC} XCDs / the kernel-trace average duration (meaningful for launches of "
+            "a millisecond or more: for short ones GRBM_GUI_ACTIVE also counts the dispatch around the kernel, so the "
+            "figure, and the MFMA busy share derived from the same count, are off);",
             f"- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {N_XCC} x {N_SIMD} SIMDs), rocprofv3's MfmaUtil "
             "expression (its own MfmaUtil value is listed beside it);",
             "- MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512;",
