@@ -327,6 +327,9 @@ dsa_status dsa_sparse_attn(const dsa_batch *b, const void *q, const void *latent
   a.D_v = D_v;
   a.sm_scale = sm_scale;
   a.splits = plan_attn_splits(b, k);
+  // the contiguous slot map addresses rows below (num_seqs - 1) * seq_stride + max_kv_len (entries past q_pos
+  // are skipped); a paged map's page ids are not known on the host
+  a.max_slots = b->page_table != nullptr ? 0 : (int64_t)(b->num_seqs - 1) * b->seq_stride + b->max_kv_len;
   return from_hip(dsa::launch_sparse_attn(a, (hipStream_t)stream), "dsa_sparse_attn launch");
 }
 

@@ -51,6 +51,7 @@ struct AttnArgs {
   int num_q, k, H, D_qk, D_v;
   float sm_scale;
   int splits;               // key-list splits per row (1 = no combine pass)
+  int64_t max_slots;        // contiguous caches: an upper bound on the slots the batch addresses; 0 = unknown
 };
 hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t s);
 size_t sparse_attn_ws_floats(int num_q, int splits, int H, int D_v);

@@ -85,6 +85,17 @@ __device__ __forceinline__ uint32_t load_lds_16_free(uint64_t src, uint32_t lds_
   return token;
 }
 
+// The same load with a 32-bit byte offset from a 64-bit base held in SGPRs (the saddr form): address = base + voff.
+__device__ __forceinline__ uint32_t load_lds_16_off(uint32_t voff, uint64_t base, uint32_t lds_base) {
+  uint32_t token;
+  asm("s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" : "=v"(token) : "v"(voff), "s"(base), "s"(lds_base));
+  return token;
+}
+__device__ __forceinline__ void load_lds_16_off_fenced(uint32_t voff, uint64_t base, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_base)
+               : "memory");
+}
+
 // S^T accumulation of the QK product in VGPRs (the builtin would put it in AGPRs, which O fills). The
 // compiler's hazard tracking does not see inside inline asm, so the wait states it would insert are spelled
 // out: two before a tile's first MFMA (a VALU write of an operand register just before it), and 20 after the
@@ -114,7 +125,9 @@ __host__ __device__ __forceinline__ size_t sparse_attn_ws_ml_offset(int num_q, i
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;   // 32-bit LDS addresses
 
-template <int H, int DQK, int DV>
+// OFF32: every selected row lies within 4 GB of the latent base, so the prologue keeps each row's byte offset
+// (slot * row bytes, 0 for the padding past the list) and a gather load adds only its chunk offset to it.
+template <int H, int DQK, int DV, bool OFF32>
 __global__ __launch_bounds__((H >= 128 ? 4 : (H + 31) / 32) * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_attn_kernel(AttnArgs a, int keys_per_split) {
   using C = AttnCfg<H, DQK, DV>;
@@ -172,7 +185,8 @@ void sparse_attn_kernel(AttnArgs a, int keys_per_split) {
 #pragma unroll
   for (int e = 0; e < PE; ++e) {
     const bool ok = ent[e] >= 0 && ent[e] <= p_r;
-    sl[e] = ok ? (uint32_t)a.slot(b, ent[e]) : 0u;
+    if constexpr (OFF32) sl[e] = ok ? (uint32_t)a.slot(b, ent[e]) * (uint32_t)C::ROWB : 0u;
+    else sl[e] = ok ? (uint32_t)a.slot(b, ent[e]) : 0u;
     msk[e] = ballot(ok);
     if (lane == 0) lds_cnt[e * C::NWAVE + wv] = (uint32_t)__popcll(msk[e]);
   }
@@ -191,7 +205,7 @@ void sparse_attn_kernel(AttnArgs a, int keys_per_split) {
   }
   __syncthreads();
   const int ntiles = (nkeys + C::BN - 1) / C::BN;
-  for (int i = nkeys + tid; i < ntiles * C::BN; i += C::NT) lds_slot[i] = ~0u;   // tail of the last tile
+  for (int i = nkeys + tid; i < ntiles * C::BN; i += C::NT) lds_slot[i] = OFF32 ? 0u : ~0u;   // tail of the last tile
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds_tile;
   // this lane's part of every tile load (loop invariant): load j fills LDS slot P = (j * NWAVE + wv) * 64 + lane,
   // i.e. row P / CPR at its swizzled chunk; packed as (row << 16) | byte offset within the row
@@ -221,11 +235,17 @@ void sparse_attn_kernel(AttnArgs a, int keys_per_split) {
   auto gather_load = [&](int t, const uint32_t (&rows)[C::PER], const uint32_t (&pk)[C::PER], int j,
                          bool fenced = false) {
     const uint32_t tile_lds = lds_base + (uint32_t)((t % C::NBUF) * C::TILE);
-    const uint64_t keep = 0ull - (uint64_t)(rows[j] != ~0u);   // arithmetic select, no branch
-    const uint64_t src = (uint64_t)latent + (((uint64_t)rows[j] * C::ROWB + (pk[j] & 0xffffu)) & keep);
     const uint32_t dst = tile_lds + (uint32_t)((j * C::NWAVE + wv) * kWave * 16);
-    if (fenced) load_lds_16(src, dst);
-    else sink ^= load_lds_16_free(src, dst);
+    if constexpr (OFF32) {
+      const uint32_t voff = rows[j] + (pk[j] & 0xffffu);
+      if (fenced) load_lds_16_off_fenced(voff, (uint64_t)latent, dst);
+      else sink ^= load_lds_16_off(voff, (uint64_t)latent, dst);
+    } else {
+      const uint64_t keep = 0ull - (uint64_t)(rows[j] != ~0u);   // arithmetic select, no branch
+      const uint64_t src = (uint64_t)latent + (((uint64_t)rows[j] * C::ROWB + (pk[j] & 0xffffu)) & keep);
+      if (fenced) load_lds_16(src, dst);
+      else sink ^= load_lds_16_free(src, dst);
+    }
   };
   // K step s of the QK block issues gather load j when s == load_step(j): the first waits two MFMAs for its row
   // address, the rest are spread evenly over the block
@@ -551,7 +571,12 @@ static hipError_t launch_t(const AttnArgs &a, hipStream_t st) {
   kps = (kps + C::BN - 1) / C::BN * C::BN;
   if (kps > C::KMAX) return hipErrorInvalidValue;   // the caller plans enough splits
   const int units = (a.num_q + 7) / 8 * 8 * C::NHG * a.splits;
-  hipLaunchKernelGGL((sparse_attn_kernel<H, DQK, DV>), dim3(units), dim3(C::NT), 0, st, a, kps);
+  // 32-bit row offsets when every slot the batch can address lies within 4 GB of the base: contiguous caches
+  // with (num_seqs - 1) * seq_stride + max_kv_len rows (the host knows it); paged caches keep 64-bit addresses
+  if (a.max_slots > 0 && a.max_slots * (int64_t)C::ROWB <= (int64_t)0xFFFFFFFFll - C::ROWB)
+    hipLaunchKernelGGL((sparse_attn_kernel<H, DQK, DV, true>), dim3(units), dim3(C::NT), 0, st, a, kps);
+  else
+    hipLaunchKernelGGL((sparse_attn_kernel<H, DQK, DV, false>), dim3(units), dim3(C::NT), 0, st, a, kps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   constexpr int HPW = 256 / (DV / 16);
