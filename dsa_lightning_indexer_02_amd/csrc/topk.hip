@@ -429,12 +429,9 @@ __device__ __forceinline__ void stream_emit_row(const float *__restrict__ row, i
 // passes count from registers, with no LDS reads between them. The passes stop as soon as the bin holding the
 // need-th key is to be kept whole: then every key >= the bin's lower bound is kept (T = that bound, all T-valued).
 constexpr int kRegItems = (kCandPerWave + kWave - 1) / kWave;   // 16
-// With `rank_above` set, `need` counts the candidates above top too (need = k): they are counted here, and if
-// they are k or more the search runs over every candidate instead.
 template <class Emit>
 __device__ __forceinline__ void regions_select_emit(const uint32_t (&ccs)[kStreamWaves], uint32_t top, uint32_t need,
-                                                    uint32_t limit, StreamShared &sh, Emit emit,
-                                                    bool rank_above = false) {
+                                                    uint32_t limit, StreamShared &sh, Emit emit) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int cb = w * kCandPerWave;
   const uint32_t cnt = ccs[w];
@@ -445,19 +442,6 @@ __device__ __forceinline__ void regions_select_emit(const uint32_t (&ccs)[kStrea
     const uint32_t j = (uint32_t)(u * kWave + lane);
     key[u] = j < cnt ? sh.cand_key[cb + j] : 0u;
     pos[u] = j < cnt ? sh.cand_pos[cb + j] : 0;
-  }
-  if (rank_above) {
-    uint32_t a = 0u;
-#pragma unroll
-    for (int u = 0; u < kRegItems; ++u) a += (uint32_t)__popcll(ballot((uint32_t)(u * kWave + lane) < cnt && key[u] > top));
-    __syncthreads();   // red is free
-    if (lane == 0) sh.red[w] = a;
-    __syncthreads();
-    uint32_t above = 0u;
-#pragma unroll
-    for (int i = 0; i < kStreamWaves; ++i) above += sh.red[i];
-    if (above >= need) top = 0xffffffffu;   // the need-th key lies above the window: search every candidate
-    else need -= above;
   }
   auto in_win = [&](int u) { return (uint32_t)(u * kWave + lane) < cnt && key[u] <= top; };
   uint32_t kmin = 0xffffffffu, kmax = 0u;
@@ -525,6 +509,109 @@ __device__ __forceinline__ void regions_select_emit(const uint32_t (&ccs)[kStrea
     const bool in = (uint32_t)(u * kWave + lane) < cnt;
     put(pos[u], key[u], in);
   }
+}
+
+// Selection of the k best among the windowed form's candidates (four wave LDS regions, as above), given the
+// row's window [lo, top]. Only candidates >= lo count: when they number k or more the row's k-th key is >= lo,
+// and then every position of the row's top-k is a candidate (a chunk keeps all its keys >= lo, or its own exact
+// top-cap when it has more than cap of them). One histogram pass over [lo, top] (kBins bins) finds the bin of
+// the k-th key; the few candidates in that bin are ranked against each other to give the exact threshold T and
+// the number of T-valued keys to take. Returns false, having emitted nothing, when the window does not settle
+// it: fewer than k candidates >= lo, k or more above top, or more than kStreamThreads candidates in the bin;
+// the caller then selects over the whole row.
+template <class Emit>
+__device__ __forceinline__ bool window_select_emit(const uint32_t (&ccs)[kStreamWaves], uint32_t lo, uint32_t top,
+                                                   uint32_t k, StreamShared &sh, Emit emit) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int cb = w * kCandPerWave;
+  const uint32_t cnt = ccs[w];
+  uint32_t key[kRegItems];
+  int32_t pos[kRegItems];
+#pragma unroll
+  for (int u = 0; u < kRegItems; ++u) {
+    const uint32_t j = (uint32_t)(u * kWave + lane);
+    key[u] = j < cnt ? sh.cand_key[cb + j] : 0u;
+    pos[u] = j < cnt ? sh.cand_pos[cb + j] : 0;
+  }
+  const uint32_t range = top - lo;   // top >= lo (both come from the same sample)
+  const int shift = range == 0u ? 0 : max(0, 32 - __clz((int)range) - kBinBits);
+  __syncthreads();   // the regions are in registers; hist, red and bcast are free
+  stream_clear_hist(sh);
+  if (tid == 0) sh.bcast[5] = 0u;
+  __syncthreads();
+  uint32_t a = 0u, in = 0u;
+#pragma unroll
+  for (int u = 0; u < kRegItems; ++u) {
+    const bool v = (uint32_t)(u * kWave + lane) < cnt;
+    const bool above = v && key[u] > top, inw = v && key[u] >= lo && key[u] <= top;
+    a += (uint32_t)__popcll(ballot(above));
+    in += (uint32_t)__popcll(ballot(inw));
+    if (inw) atomicAdd(&sh.hist[(key[u] - lo) >> shift], 1u);
+  }
+  if (lane == 0) {
+    sh.red[w] = a;
+    sh.red[kStreamWaves + w] = in;
+  }
+  __syncthreads();
+  uint32_t above = 0u, inwin = 0u;
+#pragma unroll
+  for (int i = 0; i < kStreamWaves; ++i) {
+    above += sh.red[i];
+    inwin += sh.red[kStreamWaves + i];
+  }
+  if (above >= k || above + inwin < k) return false;   // block-uniform
+  const int rr[1] = {(int)(k - above)};
+  stream_rank_bins<1>(sh, rr);   // ends with a barrier
+  const uint32_t B = sh.bcast[0], cnt_b = sh.bcast[2];
+  const uint32_t need_b = k - above - sh.bcast[1];   // 1 <= need_b <= cnt_b
+  const uint32_t blo = lo + (B << shift);
+  const uint32_t bhi = (uint32_t)min((uint64_t)top, (uint64_t)blo + ((1ull << shift) - 1ull));
+  uint32_t T, need_eq;
+  if (shift == 0 || cnt_b == need_b) {   // the bin is one key value, or it is kept whole
+    T = blo;
+    need_eq = shift == 0 ? need_b : 0xffffffffu;
+  } else {
+    if (cnt_b > (uint32_t)kStreamThreads) return false;   // block-uniform (read from bcast)
+    // the bin's keys -> a list in hist (free after the rank step), in any order; each thread then ranks one
+#pragma unroll
+    for (int u = 0; u < kRegItems; ++u) {
+      const bool v = (uint32_t)(u * kWave + lane) < cnt;
+      if (v && key[u] >= blo && key[u] <= bhi) sh.hist[atomicAdd(&sh.bcast[5], 1u)] = key[u];
+    }
+    __syncthreads();
+    if ((uint32_t)tid < cnt_b) {
+      const uint32_t x = sh.hist[tid];
+      uint32_t gt = 0u, eq = 0u;
+      for (uint32_t j = 0; j < cnt_b; ++j) {
+        const uint32_t y = sh.hist[j];
+        gt += y > x ? 1u : 0u;
+        eq += y == x ? 1u : 0u;
+      }
+      if (gt < need_b && need_b <= gt + eq) {   // x is the need_b-th largest of the bin (equal x agree)
+        sh.bcast[3] = x;
+        sh.bcast[4] = need_b - gt;
+      }
+    }
+    __syncthreads();
+    T = sh.bcast[3];
+    need_eq = sh.bcast[4];
+  }
+  uint32_t g = 0u, e = 0u;
+#pragma unroll
+  for (int u = 0; u < kRegItems; ++u) {
+    const bool v = (uint32_t)(u * kWave + lane) < cnt;
+    g += (uint32_t)__popcll(ballot(v && key[u] > T));
+    e += (uint32_t)__popcll(ballot(v && key[u] == T));
+  }
+  uint32_t base, quota;
+  stream_out_base(g, e, need_eq, sh, base, quota);
+  StreamPut<Emit> put{T, quota, base, 0u, k, emit};
+#pragma unroll
+  for (int u = 0; u < kRegItems; ++u) {
+    const bool v = (uint32_t)(u * kWave + lane) < cnt;
+    put(pos[u], key[u], v);
+  }
+  return true;
 }
 
 // Per-wave counts after stream_collect: the totals, and whether every wave's keys fit its region.
@@ -626,15 +713,18 @@ hipError_t launch_topk_rows(const float *scores, int64_t ld, const int32_t *q_po
 // streaming form's collect step over its four wave segments) and writes them, in position order, with their
 // count: a few hundred per chunk instead of k. A chunk with more than cap = min(k, chunk) such keys, or more than
 // a wave's LDS region holds, writes its own exact top-cap instead (it contains the row's top-k within that chunk
-// under the same total order). The merge pass (one workgroup per row) gathers the row's M candidates into LDS, in
-// position order, and selects k among them with the streaming form's LDS search. When M >= k the selection is
-// exact (the k-th best key is then >= lo, so every kept key is a candidate); when M < k the window missed and
-// the merge selects over the whole row from the scores instead (as does a row with too many candidates for LDS).
+// under the same total order; when the chunk's keys >= lo fit cap but not a wave's region, that top-cap also
+// holds keys below lo). The merge pass (one workgroup per row) gathers the row's M candidates into LDS, in
+// position order, and selects k among those >= lo with one histogram pass over the window (window_select_emit).
+// When k or more candidates are >= lo the selection is exact (the row's k-th best key is then >= lo, so every
+// kept key is a candidate); otherwise the window missed and the merge selects over the whole row from the scores
+// instead (as does a row with too many candidates for LDS, or a window that does not settle the threshold).
 constexpr int kWMaxChunks = kStreamThreads;   // one count per merge thread
 constexpr int kWMergeCap = kStreamWaves * kCandPerWave;
 
 // Pass 1: chunk c of row r writes its candidates at slot (r * n_chunks + c) * cap and their count at
-// cnt[r * n_chunks + c]; chunk 0 also writes the window's top at cnt[num_q * n_chunks + r]. The chunk (V * 1024 keys) is loaded into registers before the window is known: wave w
+// cnt[r * n_chunks + c]; chunk 0 also writes the window's top at cnt[num_q * n_chunks + r] and its bottom at
+// cnt[num_q * (n_chunks + 1) + r]. The chunk (V * 1024 keys) is loaded into registers before the window is known: wave w
 // holds positions w*V*256 .. (w+1)*V*256 - 1, lane l four consecutive positions per load, so lane order within a
 // load is position order.
 template <int V>
@@ -655,6 +745,8 @@ __global__ __launch_bounds__(kStreamThreads) void topk_wchunk_kernel(const float
   const int avail = (int)min((int64_t)CHUNK, ld - start);
   const bool vec = (ld & 3) == 0 && ((uintptr_t)scores & 15) == 0;
   const int wbase = w * V * 4 * kWave;
+  // the row length first: the sample loads below depend on it and need not wait behind the chunk's loads
+  const int n = q_pos[r] + 1;
   f32x4 x[V];
 #pragma unroll
   for (int u = 0; u < V; ++u) {
@@ -668,7 +760,6 @@ __global__ __launch_bounds__(kStreamThreads) void topk_wchunk_kernel(const float
       x[u].w = L + 3 < avail ? crow[L + 3] : 0.f;
     }
   }
-  const int n = q_pos[r] + 1;
   if (n <= k || start >= n) return;   // the merge pass writes rows with n <= k directly
   const int len = min(CHUNK, n - start);
   uint32_t lo, hi;
@@ -722,7 +813,10 @@ __global__ __launch_bounds__(kStreamThreads) void topk_wchunk_kernel(const float
   }
   if (tid == 0) {
     cand_cnt[(int64_t)r * n_chunks + c] = c_cand;
-    if (c == 0) cand_cnt[(int64_t)gridDim.x * n_chunks + r] = hi;   // the window's top, for the merge
+    if (c == 0) {   // the window, for the merge
+      cand_cnt[(int64_t)gridDim.x * n_chunks + r] = hi;
+      cand_cnt[(int64_t)gridDim.x * (n_chunks + 1) + r] = lo;
+    }
   }
 }
 
@@ -801,13 +895,20 @@ __global__ __launch_bounds__(kStreamThreads) void topk_wmerge_kernel(const float
     ccs[i] = (uint32_t)min(max((int)M - i * kCandPerWave, 0), kCandPerWave);
   (void)lane;
   (void)w;
-  const uint32_t top = cand_cnt[(int64_t)gridDim.x * n_chunks + r];   // written by chunk 0 of this row
-  regions_select_emit(ccs, top, (uint32_t)k, (uint32_t)k, sh, emit, true);
+  const uint32_t top = cand_cnt[(int64_t)gridDim.x * n_chunks + r];          // written by chunk 0 of this row
+  const uint32_t lo = cand_cnt[(int64_t)gridDim.x * (n_chunks + 1) + r];
+  if (!window_select_emit(ccs, lo, top, (uint32_t)k, sh, emit)) {
+    int s0, s1;
+    stream_segment_of(n, s0, s1);
+    uint32_t T, need_eq, cnt_eq;
+    stream_threshold(row, n, k, sh, T, need_eq, cnt_eq);
+    stream_emit_row(row, s0, s1, T, need_eq, (uint32_t)k, sh, emit);
+  }
 }
 
 size_t topk_windowed_ws_bytes(int num_q, int n_chunks, int cap) {
   const size_t pairs = (size_t)num_q * n_chunks * cap;
-  return (pairs * 8 + 15) / 16 * 16 + (size_t)num_q * (n_chunks + 1) * 4;   // + counts, + each row's window top
+  return (pairs * 8 + 15) / 16 * 16 + (size_t)num_q * (n_chunks + 2) * 4;   // + counts, + each row's window
 }
 
 template <int V>

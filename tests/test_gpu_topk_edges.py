@@ -153,6 +153,25 @@ def test_few_rows_adversarial_patterns(k):
     _run(s, pos, k, f"sample-miss k={k}")
 
 
+def test_few_rows_window_miss_with_region_overflow():
+    """The chunked form when the sampled window misses and a chunk overflows one wave's LDS region: the first
+    1024 positions (one region of the first 4096-key chunk) all hold the largest keys, the sampled runs hold
+    values in [0.5, 1) and every other position 0. The sample then puts the window's bottom above all but a few
+    hundred of the row's keys, so fewer than k keys reach it; the overflowing chunk writes its own top-k, whose
+    lower part lies below the window, and the selection must not take those over the other chunks' keys."""
+    k, n_q, n = 2048, 8, 32768
+    starts = (np.arange(64, dtype=np.int64) * (n - 64)) // 63
+    sampled = np.unique((starts[:, None] + np.arange(64)[None, :]).ravel())
+    rng = np.random.default_rng(77)
+    s = np.zeros((n_q, ld_for(n)), dtype=np.float32)
+    for r in range(n_q):
+        s[r, sampled] = (0.5 + 0.5 * rng.random(len(sampled))).astype(np.float32)
+        s[r, :1024] = (2.0 + rng.permutation(1024) / 4096.0).astype(np.float32)
+    pos = np.full(n_q, n - 1)
+    pos[1] = n - 7
+    _run(s, pos, k, "window miss + region overflow")
+
+
 def test_few_rows_up_to_128k():
     rng = np.random.default_rng(9)
     n_q, max_kv = 5, 1 << 17
