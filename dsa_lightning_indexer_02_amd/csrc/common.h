@@ -127,6 +127,42 @@ __device__ __forceinline__ float xor32_sum(float v) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
+// Wave-wide scans and reductions on DPP (VALU lane moves, no LDS round trip per step): row_shr 1, 2, 4, 8 build
+// the prefix within each 16-lane row; row_bcast:15 then adds row 0's (row 2's) total to row 1 (row 3), and
+// row_bcast:31 adds lanes 0..31's total to lanes 32..63. Lanes that a step does not write, or whose source lies
+// outside their row, take `id` (the operation's identity), so the same steps serve add, min and max.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v, uint32_t id, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x111, 0xf, 0xf, false));   // row_shr:1
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x112, 0xf, 0xf, false));   // row_shr:2
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x114, 0xf, 0xf, false));   // row_shr:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x118, 0xf, 0xf, false));   // row_shr:8
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x142, 0xa, 0xf, false));   // row_bcast:15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x143, 0xc, 0xf, false));   // row_bcast:31
+  return v;
+}
+struct DppAdd {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct DppMin {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+};
+struct DppMax {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+// Inclusive prefix sum over the wave, in lane order.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) { return wave_incl_scan_dpp(v, 0u, DppAdd{}); }
+// Wave totals, the same in every lane (lane 63 holds the scan's total).
+__device__ __forceinline__ uint32_t wave_total_sum(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_dpp(v, 0u, DppAdd{}), 63);
+}
+__device__ __forceinline__ uint32_t wave_total_min(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_dpp(v, 0xffffffffu, DppMin{}), 63);
+}
+__device__ __forceinline__ uint32_t wave_total_max(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_dpp(v, 0u, DppMax{}), 63);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

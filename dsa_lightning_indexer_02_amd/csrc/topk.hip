@@ -112,11 +112,7 @@ struct StreamShared {
 // Inclusive prefix sum over the 256-thread block, in thread order.
 __device__ __forceinline__ uint32_t stream_incl_scan(uint32_t v, StreamShared &sh) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+  v = wave_incl_sum(v);
   if (lane == kWave - 1) sh.wave_tot[w] = v;
   __syncthreads();
   uint32_t add = 0;
@@ -242,11 +238,7 @@ __device__ __forceinline__ uint32_t lane_prefix8(uint32_t c, uint32_t &total) {
   return (uint32_t)lanes_below(b0) + 2u * (uint32_t)lanes_below(b1) + 4u * (uint32_t)lanes_below(b2);
 }
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o);
-  return v;
-}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return wave_total_sum(v); }
 
 // ---- 1. sample: run b (0..63) starts at floor(b * (n - 64) / 63); wave w reads runs 16w .. 16w+15. Gives the
 //      window [lo, hi] (lo = 0 / hi = ~0 when the margin reaches past the sample). Uses hist, red, bcast.
@@ -267,11 +259,8 @@ __device__ __forceinline__ void stream_window(const float *__restrict__ row, int
     smin = min(smin, sk[j]);
     smax = max(smax, sk[j]);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    smin = min(smin, (uint32_t)__shfl_xor((int)smin, o));
-    smax = max(smax, (uint32_t)__shfl_xor((int)smax, o));
-  }
+  smin = wave_total_min(smin);
+  smax = wave_total_max(smax);
   stream_clear_hist(sh);
   if (lane == 0) {
     sh.red[w] = smin;
@@ -452,11 +441,8 @@ __device__ __forceinline__ void regions_select_emit(const uint32_t (&ccs)[kStrea
       kmax = max(kmax, key[u]);
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-  }
+  kmin = wave_total_min(kmin);
+  kmax = wave_total_max(kmax);
   __syncthreads();   // red and bcast are free
   if (lane == 0) {
     sh.red[w] = kmin;

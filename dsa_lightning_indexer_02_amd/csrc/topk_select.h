@@ -31,11 +31,7 @@ using TopkShared = TopkSharedT<kTopkBlock>;
 template <int BLOCK>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, TopkSharedT<BLOCK> &sh) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+  v = wave_incl_sum(v);
   if (lane == kWave - 1) sh.wave_tot[w] = v;
   __syncthreads();
   uint32_t add = 0;
@@ -80,11 +76,8 @@ __device__ __forceinline__ void select_topk(const uint32_t (&key)[ITEMS], int n,
       kmax = max(kmax, key[i]);
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-  }
+  kmin = wave_total_min(kmin);
+  kmax = wave_total_max(kmax);
   if (lane == 0) {
     sh.red[w] = kmin;
     sh.red[WAVES + w] = kmax;
