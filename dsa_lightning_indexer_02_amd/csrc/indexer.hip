@@ -204,9 +204,10 @@ struct PipeCfg {
 
 // Balanced split of a batch of few rows per sequence (decode): the key blocks of every row block (row block rb
 // has p_max(rb) / BK + 1 of them, p_max the largest position of its rows) are cut into chunks of
-// bpc = ceil(total / target) blocks, ceil(nb / bpc) chunks per row block, and workgroup u takes the u-th chunk in
-// row-block order, so a long sequence gets proportionally more workgroups than a short one. Every wave computes
-// the same split from q_pos; false for a workgroup past the last chunk.
+// bpc blocks, ceil(nb / bpc) chunks per row block, and workgroup u takes the u-th chunk in row-block order, so a
+// long sequence gets proportionally more workgroups than a short one. bpc is the smallest count from
+// ceil(total / target) up that makes at most `target` chunks in all. Every wave computes the same split from
+// q_pos; false for a workgroup past the last chunk.
 template <int ROWS, int BK>
 __device__ __forceinline__ bool balanced_unit(const IndexerArgs &a, int row_blocks, int target, int u, int &rb,
                                               int &c, int &bpc) {
@@ -225,12 +226,37 @@ __device__ __forceinline__ bool balanced_unit(const IndexerArgs &a, int row_bloc
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
     return v;
   };
-  int total = 0;
+  int total = 0, nb_max = 0;
   for (int base = 0; base < row_blocks; base += kWave) {
     const int r = base + lane;
-    total += wave_sum(r < row_blocks ? nblocks(r) : 0);
+    const int nb = r < row_blocks ? nblocks(r) : 0;
+    total += wave_sum(nb);
+    int m = nb;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
+    nb_max = max(nb_max, m);
   }
-  bpc = max(1, (total + target - 1) / target);
+  auto chunks_for = [&](int b) {   // non-increasing in b
+    int ch = 0;
+    for (int base = 0; base < row_blocks; base += kWave) {
+      const int r = base + lane;
+      ch += wave_sum(r < row_blocks ? (nblocks(r) + b - 1) / b : 0);
+    }
+    return ch;
+  };
+  // ceil(total / target) blocks per chunk can still leave a few more than `target` chunks (each row block rounds
+  // up), and those would run as a second round of workgroups after the first: take the smallest bpc that fits,
+  // by bisection up to nb_max (one chunk per row block, the fewest there can be)
+  int b_lo = max(1, (total + target - 1) / target);
+  bpc = b_lo;
+  if (b_lo < nb_max && chunks_for(b_lo) > target) {
+    int b_hi = nb_max;   // chunks_for(b_lo) > target; b_hi fits, or nothing does
+    while (b_hi - b_lo > 1) {
+      const int mid = (b_lo + b_hi) / 2;
+      if (chunks_for(mid) <= target) b_hi = mid; else b_lo = mid;
+    }
+    bpc = b_hi;
+  }
   int before = 0;
   for (int base = 0; base < row_blocks; base += kWave) {
     const int r = base + lane;
