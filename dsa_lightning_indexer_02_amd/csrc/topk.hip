@@ -100,44 +100,50 @@ constexpr int kSample = kRuns * kRun;      // 4096 sampled keys per row
 constexpr int kBinsPerThread = kBins / kStreamThreads;
 constexpr int kCandPerWave = 1016;         // candidate (key, position) pairs one wave keeps: 4 workgroups per CU
 
-struct StreamShared {
+// Shared state of a W-wave workgroup: the same candidate capacity in all (W regions of CPW pairs).
+template <int W>
+struct StreamSharedT {
+  static constexpr int CPW = kStreamWaves * kCandPerWave / W;   // candidate pairs per wave region
   uint32_t hist[kBins];
-  uint32_t cand_key[kStreamWaves * kCandPerWave];
-  int32_t cand_pos[kStreamWaves * kCandPerWave];
-  uint32_t wave_tot[kStreamWaves];
-  uint32_t red[4 * kStreamWaves];
+  uint32_t cand_key[W * CPW];
+  int32_t cand_pos[W * CPW];
+  uint32_t wave_tot[W];
+  uint32_t red[4 * W];
   uint32_t bcast[6];
 };
+using StreamShared = StreamSharedT<kStreamWaves>;
 
-// Inclusive prefix sum over the 256-thread block, in thread order.
-__device__ __forceinline__ uint32_t stream_incl_scan(uint32_t v, StreamShared &sh) {
+// Inclusive prefix sum over the block, in thread order.
+template <int W>
+__device__ __forceinline__ uint32_t stream_incl_scan(uint32_t v, StreamSharedT<W> &sh) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   v = wave_incl_sum(v);
   if (lane == kWave - 1) sh.wave_tot[w] = v;
   __syncthreads();
   uint32_t add = 0;
 #pragma unroll
-  for (int i = 0; i < kStreamWaves; ++i) add += i < w ? sh.wave_tot[i] : 0u;
+  for (int i = 0; i < W; ++i) add += i < w ? sh.wave_tot[i] : 0u;
   __syncthreads();
   return v + add;
 }
 
 // Bins counted from the top (bin kBins-1 first). For each rank r[q] (1-based, 1 <= r[q] <= total), writes
 // to sh.bcast[3q..3q+2] the bin holding the r[q]-th key, the number of keys in higher bins, and its count.
-template <int NR>
-__device__ __forceinline__ void stream_rank_bins(StreamShared &sh, const int (&r)[NR]) {
+template <int NR, int W>
+__device__ __forceinline__ void stream_rank_bins(StreamSharedT<W> &sh, const int (&r)[NR]) {
+  constexpr int BPT = kBins / (W * kWave);              // bins per thread
   const int tid = threadIdx.x;
-  const int top = kBins - 1 - kBinsPerThread * tid;     // this thread's bins: top, top-1, .., top-7
-  uint32_t c[kBinsPerThread], sum = 0;
+  const int top = kBins - 1 - BPT * tid;                // this thread's bins: top, top-1, .., top-BPT+1
+  uint32_t c[BPT], sum = 0;
 #pragma unroll
-  for (int j = 0; j < kBinsPerThread; ++j) {
+  for (int j = 0; j < BPT; ++j) {
     c[j] = sh.hist[top - j];
     sum += c[j];
   }
   const uint32_t incl = stream_incl_scan(sum, sh);
   uint32_t above = incl - sum;
 #pragma unroll
-  for (int j = 0; j < kBinsPerThread; ++j) {
+  for (int j = 0; j < BPT; ++j) {
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
       if (above < (uint32_t)r[q] && (uint32_t)r[q] <= above + c[j]) {
@@ -151,13 +157,15 @@ __device__ __forceinline__ void stream_rank_bins(StreamShared &sh, const int (&r
   __syncthreads();
 }
 
-__device__ __forceinline__ void stream_clear_hist(StreamShared &sh) {
-  for (int b = threadIdx.x; b < kBins; b += kStreamThreads) sh.hist[b] = 0u;
+template <int W>
+__device__ __forceinline__ void stream_clear_hist(StreamSharedT<W> &sh) {
+  for (int b = threadIdx.x; b < kBins; b += W * kWave) sh.hist[b] = 0u;
 }
 
 // The k-th largest key of the whole row by streaming bucket passes over the row (exact; used when the sampled
 // window misses). Bins cover the key bits 31..21, then 20..10, then 9..0 of the window.
-__device__ __forceinline__ void stream_threshold(const float *__restrict__ row, int n, int k, StreamShared &sh,
+template <int W>
+__device__ __forceinline__ void stream_threshold(const float *__restrict__ row, int n, int k, StreamSharedT<W> &sh,
                                                  uint32_t &T, uint32_t &need_eq, uint32_t &cnt_eq) {
   const int tid = threadIdx.x;
   uint32_t lo = 0u, hi = 0xffffffffu, need = (uint32_t)k;
@@ -166,7 +174,7 @@ __device__ __forceinline__ void stream_threshold(const float *__restrict__ row, 
     __syncthreads();
     stream_clear_hist(sh);
     __syncthreads();
-    for (int L = tid; L < n; L += kStreamThreads) {
+    for (int L = tid; L < n; L += W * kWave) {
       const uint32_t x = order_key(row[L]);
       if (x >= lo && x <= hi) atomicAdd(&sh.hist[(x - lo) >> shift], 1u);
     }
@@ -353,21 +361,22 @@ __device__ __forceinline__ void stream_collect(const float *__restrict__ row, in
 // Output slots of the kept keys: keys > T, and the first need_eq T-valued keys in position order (wave order,
 // then in order within a wave). gt_w / eq_w: this wave's counts. Gives the wave's first slot and how many of its
 // T-valued keys it takes. Starts with a barrier (red is reused).
-__device__ __forceinline__ void stream_out_base(uint32_t gt_w, uint32_t eq_w, uint32_t need_eq, StreamShared &sh,
+template <int W>
+__device__ __forceinline__ void stream_out_base(uint32_t gt_w, uint32_t eq_w, uint32_t need_eq, StreamSharedT<W> &sh,
                                                 uint32_t &base, uint32_t &quota) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   __syncthreads();
   if (lane == 0) {
     sh.red[w] = gt_w;
-    sh.red[kStreamWaves + w] = eq_w;
+    sh.red[W + w] = eq_w;
   }
   __syncthreads();
   uint32_t eq_before = 0u;
   base = 0u;
 #pragma unroll
-  for (int i = 0; i < kStreamWaves; ++i) {
+  for (int i = 0; i < W; ++i) {
     if (i < w) {
-      const uint32_t ei = sh.red[kStreamWaves + i];
+      const uint32_t ei = sh.red[W + i];
       const uint32_t take_i = min(ei, need_eq > eq_before ? need_eq - eq_before : 0u);
       base += sh.red[i] + take_i;
       eq_before += ei;
@@ -397,9 +406,9 @@ struct StreamPut {
 };
 
 // Emit the kept keys of this wave's row segment [s0, s1), read again from the scores.
-template <class Emit>
+template <class Emit, int W>
 __device__ __forceinline__ void stream_emit_row(const float *__restrict__ row, int s0, int s1, uint32_t T,
-                                                uint32_t need_eq, uint32_t limit, StreamShared &sh, Emit emit) {
+                                                uint32_t need_eq, uint32_t limit, StreamSharedT<W> &sh, Emit emit) {
   uint32_t g = 0u, e = 0u;
   stream_segment(row, s0, s1, [&](int, uint32_t x, bool valid) {
     g += (uint32_t)__popcll(ballot(valid && x > T));
@@ -505,16 +514,17 @@ __device__ __forceinline__ void regions_select_emit(const uint32_t (&ccs)[kStrea
 // the number of T-valued keys to take. Returns false, having emitted nothing, when the window does not settle
 // it: fewer than k candidates >= lo, k or more above top, or more than kStreamThreads candidates in the bin;
 // the caller then selects over the whole row.
-template <class Emit>
-__device__ __forceinline__ bool window_select_emit(const uint32_t (&ccs)[kStreamWaves], uint32_t lo, uint32_t top,
-                                                   uint32_t k, StreamShared &sh, Emit emit) {
+template <class Emit, int W>
+__device__ __forceinline__ bool window_select_emit(const uint32_t (&ccs)[W], uint32_t lo, uint32_t top,
+                                                   uint32_t k, StreamSharedT<W> &sh, Emit emit) {
+  constexpr int CPW = StreamSharedT<W>::CPW, ITEMS = (CPW + kWave - 1) / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const int cb = w * kCandPerWave;
+  const int cb = w * CPW;
   const uint32_t cnt = ccs[w];
-  uint32_t key[kRegItems];
-  int32_t pos[kRegItems];
+  uint32_t key[ITEMS];
+  int32_t pos[ITEMS];
 #pragma unroll
-  for (int u = 0; u < kRegItems; ++u) {
+  for (int u = 0; u < ITEMS; ++u) {
     const uint32_t j = (uint32_t)(u * kWave + lane);
     key[u] = j < cnt ? sh.cand_key[cb + j] : 0u;
     pos[u] = j < cnt ? sh.cand_pos[cb + j] : 0;
@@ -527,7 +537,7 @@ __device__ __forceinline__ bool window_select_emit(const uint32_t (&ccs)[kStream
   __syncthreads();
   uint32_t a = 0u, in = 0u;
 #pragma unroll
-  for (int u = 0; u < kRegItems; ++u) {
+  for (int u = 0; u < ITEMS; ++u) {
     const bool v = (uint32_t)(u * kWave + lane) < cnt;
     const bool above = v && key[u] > top, inw = v && key[u] >= lo && key[u] <= top;
     a += (uint32_t)__popcll(ballot(above));
@@ -536,14 +546,14 @@ __device__ __forceinline__ bool window_select_emit(const uint32_t (&ccs)[kStream
   }
   if (lane == 0) {
     sh.red[w] = a;
-    sh.red[kStreamWaves + w] = in;
+    sh.red[W + w] = in;
   }
   __syncthreads();
   uint32_t above = 0u, inwin = 0u;
 #pragma unroll
-  for (int i = 0; i < kStreamWaves; ++i) {
+  for (int i = 0; i < W; ++i) {
     above += sh.red[i];
-    inwin += sh.red[kStreamWaves + i];
+    inwin += sh.red[W + i];
   }
   if (above >= k || above + inwin < k) return false;   // block-uniform
   const int rr[1] = {(int)(k - above)};
@@ -557,10 +567,10 @@ __device__ __forceinline__ bool window_select_emit(const uint32_t (&ccs)[kStream
     T = blo;
     need_eq = shift == 0 ? need_b : 0xffffffffu;
   } else {
-    if (cnt_b > (uint32_t)kStreamThreads) return false;   // block-uniform (read from bcast)
+    if (cnt_b > (uint32_t)(W * kWave)) return false;   // block-uniform (read from bcast)
     // the bin's keys -> a list in hist (free after the rank step), in any order; each thread then ranks one
 #pragma unroll
-    for (int u = 0; u < kRegItems; ++u) {
+    for (int u = 0; u < ITEMS; ++u) {
       const bool v = (uint32_t)(u * kWave + lane) < cnt;
       if (v && key[u] >= blo && key[u] <= bhi) sh.hist[atomicAdd(&sh.bcast[5], 1u)] = key[u];
     }
@@ -584,7 +594,7 @@ __device__ __forceinline__ bool window_select_emit(const uint32_t (&ccs)[kStream
   }
   uint32_t g = 0u, e = 0u;
 #pragma unroll
-  for (int u = 0; u < kRegItems; ++u) {
+  for (int u = 0; u < ITEMS; ++u) {
     const bool v = (uint32_t)(u * kWave + lane) < cnt;
     g += (uint32_t)__popcll(ballot(v && key[u] > T));
     e += (uint32_t)__popcll(ballot(v && key[u] == T));
@@ -593,7 +603,7 @@ __device__ __forceinline__ bool window_select_emit(const uint32_t (&ccs)[kStream
   stream_out_base(g, e, need_eq, sh, base, quota);
   StreamPut<Emit> put{T, quota, base, 0u, k, emit};
 #pragma unroll
-  for (int u = 0; u < kRegItems; ++u) {
+  for (int u = 0; u < ITEMS; ++u) {
     const bool v = (uint32_t)(u * kWave + lane) < cnt;
     put(pos[u], key[u], v);
   }
@@ -622,10 +632,11 @@ __device__ __forceinline__ void stream_counts(uint32_t ca, uint32_t cc, StreamSh
   }
 }
 
-// Segments of the 4 waves over [0, n): starts at multiples of 256 positions (16-byte aligned when the row is).
+// Segments of the W waves over [0, n): starts at multiples of 256 positions (16-byte aligned when the row is).
+template <int W = kStreamWaves>
 __device__ __forceinline__ void stream_segment_of(int n, int &s0, int &s1) {
   const int w = threadIdx.x / kWave;
-  const int seg = ((n + kStreamWaves - 1) / kStreamWaves + 4 * kWave - 1) / (4 * kWave) * (4 * kWave);
+  const int seg = ((n + W - 1) / W + 4 * kWave - 1) / (4 * kWave) * (4 * kWave);
   s0 = min(n, w * seg);
   s1 = min(n, s0 + seg);
 }
@@ -707,6 +718,9 @@ hipError_t launch_topk_rows(const float *scores, int64_t ld, const int32_t *q_po
 // instead (as does a row with too many candidates for LDS, or a window that does not settle the threshold).
 constexpr int kWMaxChunks = kStreamThreads;   // one count per merge thread
 constexpr int kWMergeCap = kStreamWaves * kCandPerWave;
+// The merge runs 16 waves: its steps are short chains of barriers, ballots and per-item loops, and four times
+// the waves give each lane a quarter of the candidate items.
+constexpr int kMergeWaves = 16;
 
 // Pass 1: chunk c of row r writes its candidates at slot (r * n_chunks + c) * cap and their count at
 // cnt[r * n_chunks + c]; chunk 0 also writes the window's top at cnt[num_q * n_chunks + r] and its bottom at
@@ -808,22 +822,25 @@ __global__ __launch_bounds__(kStreamThreads) void topk_wchunk_kernel(const float
 
 // Pass 2: one workgroup per row selects k among its M candidates (or, when M < k or M exceeds the LDS regions,
 // over the whole row).
-__global__ __launch_bounds__(kStreamThreads) void topk_wmerge_kernel(const float *__restrict__ scores, int64_t ld,
+template <int W>
+__global__ __launch_bounds__(W * kWave) void topk_wmerge_kernel(const float *__restrict__ scores, int64_t ld,
                                                                      const int32_t *__restrict__ q_pos, int k,
                                                                      int chunk, int n_chunks, int cap,
                                                                      const uint32_t *__restrict__ cand_key,
                                                                      const int32_t *__restrict__ cand_pos,
                                                                      const uint32_t *__restrict__ cand_cnt,
                                                                      int32_t *__restrict__ idx) {
-  __shared__ StreamShared sh;
+  constexpr int NT = W * kWave, CPW = StreamSharedT<W>::CPW;
+  static_assert(NT >= kWMaxChunks, "one count per thread");
+  __shared__ StreamSharedT<W> sh;
   __shared__ uint32_t pre[kWMaxChunks + 1];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int r = blockIdx.x, tid = threadIdx.x;
   // the counts are loaded with q_pos (chunks past the row's end are masked once n is known)
   const uint32_t v_raw = tid < n_chunks ? cand_cnt[(int64_t)r * n_chunks + tid] : 0u;
   const int n = q_pos[r] + 1;
   int32_t *out = idx + (int64_t)r * k;
   if (n <= k) {
-    for (int j = tid; j < k; j += kStreamThreads) out[j] = j < n ? j : -1;
+    for (int j = tid; j < k; j += NT) out[j] = j < n ? j : -1;
     return;
   }
   const int used = (n + chunk - 1) / chunk;   // <= n_chunks <= kWMaxChunks
@@ -837,7 +854,7 @@ __global__ __launch_bounds__(kStreamThreads) void topk_wmerge_kernel(const float
   auto emit = [&](uint32_t slot, int L, uint32_t) { out[slot] = L; };
   if (M < (uint32_t)k || M > (uint32_t)kWMergeCap) {
     int s0, s1;
-    stream_segment_of(n, s0, s1);
+    stream_segment_of<W>(n, s0, s1);
     uint32_t T, need_eq, cnt_eq;
     stream_threshold(row, n, k, sh, T, need_eq, cnt_eq);
     stream_emit_row(row, s0, s1, T, need_eq, (uint32_t)k, sh, emit);
@@ -846,12 +863,12 @@ __global__ __launch_bounds__(kStreamThreads) void topk_wmerge_kernel(const float
   // candidates -> LDS, flat in position order (chunk order, then order within the chunk); every load is issued
   // before the first store, so the row pays one memory latency
   const int64_t base = (int64_t)r * n_chunks * cap;
-  constexpr int PM = (kWMergeCap + kStreamThreads - 1) / kStreamThreads;
+  constexpr int PM = (kWMergeCap + NT - 1) / NT;
   uint32_t mk[PM];
   int32_t mp[PM];
 #pragma unroll
   for (int u = 0; u < PM; ++u) {
-    const uint32_t j = (uint32_t)(u * kStreamThreads + tid);
+    const uint32_t j = (uint32_t)(u * NT + tid);
     mk[u] = 0u;
     mp[u] = 0;
     if (j < M) {
@@ -867,25 +884,22 @@ __global__ __launch_bounds__(kStreamThreads) void topk_wmerge_kernel(const float
   }
 #pragma unroll
   for (int u = 0; u < PM; ++u) {
-    const uint32_t j = (uint32_t)(u * kStreamThreads + tid);
+    const uint32_t j = (uint32_t)(u * NT + tid);
     if (j < M) {
       sh.cand_key[j] = mk[u];
       sh.cand_pos[j] = mp[u];
     }
   }
   __syncthreads();
-  // the flat array seen as the four wave regions of the streaming form
-  uint32_t ccs[kStreamWaves];
+  // the flat array seen as W wave regions of CPW pairs
+  uint32_t ccs[W];
 #pragma unroll
-  for (int i = 0; i < kStreamWaves; ++i)
-    ccs[i] = (uint32_t)min(max((int)M - i * kCandPerWave, 0), kCandPerWave);
-  (void)lane;
-  (void)w;
+  for (int i = 0; i < W; ++i) ccs[i] = (uint32_t)min(max((int)M - i * CPW, 0), CPW);
   const uint32_t top = cand_cnt[(int64_t)gridDim.x * n_chunks + r];          // written by chunk 0 of this row
   const uint32_t lo = cand_cnt[(int64_t)gridDim.x * (n_chunks + 1) + r];
   if (!window_select_emit(ccs, lo, top, (uint32_t)k, sh, emit)) {
     int s0, s1;
-    stream_segment_of(n, s0, s1);
+    stream_segment_of<W>(n, s0, s1);
     uint32_t T, need_eq, cnt_eq;
     stream_threshold(row, n, k, sh, T, need_eq, cnt_eq);
     stream_emit_row(row, s0, s1, T, need_eq, (uint32_t)k, sh, emit);
@@ -920,8 +934,8 @@ hipError_t launch_topk_windowed(const float *scores, int64_t ld, const int32_t *
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_wmerge_kernel, dim3(num_q), dim3(kStreamThreads), 0, s, scores, ld, q_pos, k, chunk,
-                     n_chunks, cap, ck, cp, cc, idx);
+  hipLaunchKernelGGL(topk_wmerge_kernel<kMergeWaves>, dim3(num_q), dim3(kMergeWaves * kWave), 0, s, scores, ld, q_pos,
+                     k, chunk, n_chunks, cap, ck, cp, cc, idx);
   return hipGetLastError();
 }
 
