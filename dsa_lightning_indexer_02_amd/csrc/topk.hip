@@ -248,12 +248,13 @@ __device__ __forceinline__ uint32_t lane_prefix8(uint32_t c, uint32_t &total) {
 
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return wave_total_sum(v); }
 
-// ---- 1. sample: run b (0..63) starts at floor(b * (n - 64) / 63); wave w reads runs 16w .. 16w+15. Gives the
-//      window [lo, hi] (lo = 0 / hi = ~0 when the margin reaches past the sample). Uses hist, red, bcast.
-__device__ __forceinline__ void stream_window(const float *__restrict__ row, int n, int k, StreamShared &sh,
+// ---- 1. sample: run b (0..63) starts at floor(b * (n - 64) / 63); wave w of W reads runs w*64/W .. (w+1)*64/W - 1.
+//      Gives the window [lo, hi] (lo = 0 / hi = ~0 when the margin reaches past the sample). Uses hist, red, bcast.
+template <int W>
+__device__ __forceinline__ void stream_window(const float *__restrict__ row, int n, int k, StreamSharedT<W> &sh,
                                               uint32_t &lo, uint32_t &hi) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  constexpr int SP = kSample / kStreamThreads;
+  constexpr int SP = kSample / (W * kWave);   // sample runs per wave
   uint32_t sk[SP];
 #pragma unroll
   for (int j = 0; j < SP; ++j) {
@@ -272,15 +273,15 @@ __device__ __forceinline__ void stream_window(const float *__restrict__ row, int
   stream_clear_hist(sh);
   if (lane == 0) {
     sh.red[w] = smin;
-    sh.red[kStreamWaves + w] = smax;
+    sh.red[W + w] = smax;
   }
   __syncthreads();
   smin = sh.red[0];
-  smax = sh.red[kStreamWaves];
+  smax = sh.red[W];
 #pragma unroll
-  for (int i = 1; i < kStreamWaves; ++i) {
+  for (int i = 1; i < W; ++i) {
     smin = min(smin, sh.red[i]);
-    smax = max(smax, sh.red[kStreamWaves + i]);
+    smax = max(smax, sh.red[W + i]);
   }
   const uint32_t range = smax - smin;
   const int shift = range == 0u ? 0 : max(0, 32 - __clz((int)range) - kBinBits);
@@ -611,24 +612,25 @@ __device__ __forceinline__ bool window_select_emit(const uint32_t (&ccs)[W], uin
 }
 
 // Per-wave counts after stream_collect: the totals, and whether every wave's keys fit its region.
-__device__ __forceinline__ void stream_counts(uint32_t ca, uint32_t cc, StreamShared &sh, uint32_t (&ccs)[kStreamWaves],
+template <int W>
+__device__ __forceinline__ void stream_counts(uint32_t ca, uint32_t cc, StreamSharedT<W> &sh, uint32_t (&ccs)[W],
                                               uint32_t &c_above, uint32_t &c_cand, bool &fits) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   __syncthreads();   // bcast and red are free again
   if (lane == 0) {
     sh.red[w] = ca;
-    sh.red[kStreamWaves + w] = cc;
+    sh.red[W + w] = cc;
   }
   __syncthreads();
   c_above = 0u;
   c_cand = 0u;
   fits = true;
 #pragma unroll
-  for (int i = 0; i < kStreamWaves; ++i) {
-    ccs[i] = sh.red[kStreamWaves + i];
+  for (int i = 0; i < W; ++i) {
+    ccs[i] = sh.red[W + i];
     c_above += sh.red[i];
     c_cand += ccs[i];
-    fits = fits && ccs[i] <= (uint32_t)kCandPerWave;
+    fits = fits && ccs[i] <= (uint32_t)StreamSharedT<W>::CPW;
   }
 }
 
@@ -721,21 +723,24 @@ constexpr int kWMergeCap = kStreamWaves * kCandPerWave;
 // The merge runs 16 waves: its steps are short chains of barriers, ballots and per-item loops, and four times
 // the waves give each lane a quarter of the candidate items.
 constexpr int kMergeWaves = 16;
+// The chunk pass: waves per workgroup (its chunk of V * 4 * 64 keys per wave stays in registers).
+constexpr int kChunkWaves = 16;
 
 // Pass 1: chunk c of row r writes its candidates at slot (r * n_chunks + c) * cap and their count at
 // cnt[r * n_chunks + c]; chunk 0 also writes the window's top at cnt[num_q * n_chunks + r] and its bottom at
-// cnt[num_q * (n_chunks + 1) + r]. The chunk (V * 1024 keys) is loaded into registers before the window is known: wave w
-// holds positions w*V*256 .. (w+1)*V*256 - 1, lane l four consecutive positions per load, so lane order within a
-// load is position order.
-template <int V>
-__global__ __launch_bounds__(kStreamThreads) void topk_wchunk_kernel(const float *__restrict__ scores, int64_t ld,
+// cnt[num_q * (n_chunks + 1) + r]. The chunk (V * 256 keys per wave) is loaded into registers before the window is
+// known: wave w holds positions w*V*256 .. (w+1)*V*256 - 1, lane l four consecutive positions per load, so lane
+// order within a load is position order.
+template <int V, int W>
+__global__ __launch_bounds__(W * kWave) void topk_wchunk_kernel(const float *__restrict__ scores, int64_t ld,
                                                                      const int32_t *__restrict__ q_pos, int k,
                                                                      int n_chunks, int cap,
                                                                      uint32_t *__restrict__ cand_key,
                                                                      int32_t *__restrict__ cand_pos,
                                                                      uint32_t *__restrict__ cand_cnt) {
-  constexpr int CHUNK = V * 4 * kStreamThreads;
-  __shared__ StreamShared sh;
+  constexpr int CHUNK = V * 4 * W * kWave, CPW = StreamSharedT<W>::CPW;
+  static_assert(V >= 1, "a chunk holds at least one 16-byte load per lane");
+  __shared__ StreamSharedT<W> sh;
   const int r = blockIdx.x, c = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int start = c * CHUNK;
@@ -765,7 +770,7 @@ __global__ __launch_bounds__(kStreamThreads) void topk_wchunk_kernel(const float
   uint32_t lo, hi;
   stream_window(row, n, k, sh, lo, hi);
   // keys >= lo of this wave's positions -> its LDS region, in position order
-  const int cb = w * kCandPerWave;
+  const int cb = w * CPW;
   uint32_t cc = 0u;
 #pragma unroll
   for (int u = 0; u < V; ++u) {
@@ -779,7 +784,7 @@ __global__ __launch_bounds__(kStreamThreads) void topk_wchunk_kernel(const float
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (L + j < len && kx[j] >= lo) {
-        if (slot < (uint32_t)kCandPerWave) {
+        if (slot < (uint32_t)CPW) {
           sh.cand_key[cb + slot] = kx[j];
           sh.cand_pos[cb + slot] = L + j;
         }
@@ -788,21 +793,21 @@ __global__ __launch_bounds__(kStreamThreads) void topk_wchunk_kernel(const float
     }
     cc += tot;
   }
-  uint32_t ccs[kStreamWaves], c_above, c_cand;
+  uint32_t ccs[W], c_above, c_cand;
   bool fits;
   stream_counts(0u, cc, sh, ccs, c_above, c_cand, fits);
   const int64_t dst = ((int64_t)r * n_chunks + c) * cap;
   if (fits && c_cand <= (uint32_t)cap) {
     uint32_t base = 0u;
 #pragma unroll
-    for (int i = 0; i < kStreamWaves; ++i) base += i < w ? ccs[i] : 0u;
+    for (int i = 0; i < W; ++i) base += i < w ? ccs[i] : 0u;
     for (uint32_t i = lane; i < cc; i += kWave) {
       cand_key[dst + base + i] = sh.cand_key[cb + i];
       cand_pos[dst + base + i] = start + sh.cand_pos[cb + i];
     }
   } else {   // the chunk's own exact top-cap, by streaming bucket passes over its scores (rare)
     int s0, s1;
-    stream_segment_of(len, s0, s1);
+    stream_segment_of<W>(len, s0, s1);
     uint32_t T, need_eq, cnt_eq;
     stream_threshold(crow, len, cap, sh, T, need_eq, cnt_eq);
     stream_emit_row(crow, s0, s1, T, need_eq, (uint32_t)cap, sh, [&](uint32_t slot, int L, uint32_t xk) {
@@ -914,8 +919,8 @@ size_t topk_windowed_ws_bytes(int num_q, int n_chunks, int cap) {
 template <int V>
 static void launch_wchunk(const float *scores, int64_t ld, const int32_t *q_pos, int num_q, int k, int n_chunks, int cap,
                           uint32_t *ck, int32_t *cp, uint32_t *cc, hipStream_t s) {
-  hipLaunchKernelGGL(topk_wchunk_kernel<V>, dim3(num_q, n_chunks), dim3(kStreamThreads), 0, s, scores, ld, q_pos, k,
-                     n_chunks, cap, ck, cp, cc);
+  hipLaunchKernelGGL((topk_wchunk_kernel<V, kChunkWaves>), dim3(num_q, n_chunks), dim3(kChunkWaves * kWave), 0, s,
+                     scores, ld, q_pos, k, n_chunks, cap, ck, cp, cc);
 }
 
 hipError_t launch_topk_windowed(const float *scores, int64_t ld, const int32_t *q_pos, int num_q, int k, int chunk,
@@ -927,9 +932,9 @@ hipError_t launch_topk_windowed(const float *scores, int64_t ld, const int32_t *
   int32_t *cp = reinterpret_cast<int32_t *>(ck + pairs);
   uint32_t *cc = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) + (pairs * 8 + 15) / 16 * 16);
   switch (chunk) {
-    case 4096: launch_wchunk<4>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
-    case 8192: launch_wchunk<8>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
-    case 16384: launch_wchunk<16>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
+    case 4096: launch_wchunk<4096 / (4 * kChunkWaves * kWave)>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
+    case 8192: launch_wchunk<8192 / (4 * kChunkWaves * kWave)>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
+    case 16384: launch_wchunk<16384 / (4 * kChunkWaves * kWave)>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
