@@ -221,27 +221,22 @@ __device__ __forceinline__ bool balanced_unit(const IndexerArgs &a, int row_bloc
     }
     return p < 0 ? 0 : p / BK + 1;
   };
-  auto wave_sum = [](int v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+  // the block counts of the first 64 row blocks stay in a register (a decode batch rarely has more), so the
+  // passes below pay one load latency, not one each; the wave reductions and scans run on DPP
+  const int nb0 = lane < row_blocks ? nblocks(lane) : 0;
+  auto nb_of = [&](int base) {
+    const int r = base + lane;
+    return base == 0 ? nb0 : (r < row_blocks ? nblocks(r) : 0);
   };
   int total = 0, nb_max = 0;
   for (int base = 0; base < row_blocks; base += kWave) {
-    const int r = base + lane;
-    const int nb = r < row_blocks ? nblocks(r) : 0;
-    total += wave_sum(nb);
-    int m = nb;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
-    nb_max = max(nb_max, m);
+    const int nb = nb_of(base);
+    total += (int)wave_total_sum((uint32_t)nb);
+    nb_max = max(nb_max, (int)wave_total_max((uint32_t)nb));
   }
   auto chunks_for = [&](int b) {   // non-increasing in b
     int ch = 0;
-    for (int base = 0; base < row_blocks; base += kWave) {
-      const int r = base + lane;
-      ch += wave_sum(r < row_blocks ? (nblocks(r) + b - 1) / b : 0);
-    }
+    for (int base = 0; base < row_blocks; base += kWave) ch += (int)wave_total_sum((uint32_t)((nb_of(base) + b - 1) / b));
     return ch;
   };
   // ceil(total / target) blocks per chunk can still leave a few more than `target` chunks (each row block rounds
@@ -260,21 +255,16 @@ __device__ __forceinline__ bool balanced_unit(const IndexerArgs &a, int row_bloc
   int before = 0;
   for (int base = 0; base < row_blocks; base += kWave) {
     const int r = base + lane;
-    const int ch = r < row_blocks ? (nblocks(r) + bpc - 1) / bpc : 0;
-    int incl = ch;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
+    const int ch = (nb_of(base) + bpc - 1) / bpc;
+    const int incl = (int)wave_incl_sum((uint32_t)ch);
     const uint64_t m = ballot(ch > 0 && u >= before + incl - ch && u < before + incl);
     if (m != 0) {
-      const int src = __ffsll((unsigned long long)m) - 1;
-      rb = __shfl(r, src);
-      c = u - (before + __shfl(incl - ch, src));
+      const int src = __ffsll((unsigned long long)m) - 1;   // wave-uniform
+      rb = __builtin_amdgcn_readlane(r, src);
+      c = u - (before + __builtin_amdgcn_readlane(incl - ch, src));
       return true;
     }
-    before += __shfl(incl, kWave - 1);
+    before += __builtin_amdgcn_readlane(incl, kWave - 1);
   }
   return false;
 }
