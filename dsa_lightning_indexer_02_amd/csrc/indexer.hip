@@ -169,7 +169,7 @@ __global__ __launch_bounds__(NW * kWave) void indexer_kernel(IndexerArgs a, int 
           for (int t = 0; t < C::MT; ++t)
 #pragma unroll
             for (int i = 0; i < 16; ++i) part = fmaf(wr[t][i], relu(acc[t][i]), part);
-          part += __shfl_xor(part, 32);
+          part = xor32_sum(part);   // own + other half-wave (v_permlane32_swap)
           const int s = s0 + n;
           if (g == 0 && s <= my_p) {
             if constexpr (FP8) part *= lds_sig[grp * 32 + n];
@@ -425,7 +425,7 @@ __global__ __launch_bounds__((NW + 1) * kWave) void indexer_pipe_kernel(IndexerA
             for (int t = 0; t < C::MT; ++t)
 #pragma unroll
               for (int i = 0; i < 16; ++i) part = fmaf(wr[t][i], relu(acc[t][i]), part);
-            part += __shfl_xor(part, 32);
+            part = xor32_sum(part);   // own + other half-wave (v_permlane32_swap)
             const int s = s0 + n;
             if (g == 0 && s <= my_p) a.scores[(int64_t)my_row * a.ld + s] = part * sig;
           }
@@ -787,7 +787,7 @@ __global__ __launch_bounds__(ft::NT) void indexer_topk_kernel(IndexerArgs a, int
       for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) part = fmaf(wr[t][i], relu(acc[t][i]), part);
-      part += __shfl_xor(part, 32);
+      part = xor32_sum(part);   // own + other half-wave (v_permlane32_swap)
       const int sk = start + s0 + nn;
       if (g == 0 && sk <= p) {
         if constexpr (FP8) part *= a.k_scale[a.slot(b, sk)];
