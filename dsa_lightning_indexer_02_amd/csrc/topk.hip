@@ -97,7 +97,6 @@ constexpr int kStreamUnroll4 = 8;          // 16-byte loads in flight per wave (
 constexpr int kRun = kWave;                // sample runs of 64 consecutive keys
 constexpr int kRuns = 64;
 constexpr int kSample = kRuns * kRun;      // 4096 sampled keys per row
-constexpr int kBinsPerThread = kBins / kStreamThreads;
 constexpr int kCandPerWave = 1016;         // candidate (key, position) pairs one wave keeps: 4 workgroups per CU
 
 // Shared state of a W-wave workgroup: the same candidate capacity in all (W regions of CPW pairs).
@@ -507,13 +506,13 @@ __device__ __forceinline__ void regions_select_emit(const uint32_t (&ccs)[kStrea
   }
 }
 
-// Selection of the k best among the windowed form's candidates (four wave LDS regions, as above), given the
+// Selection of the k best among the windowed form's candidates (W wave LDS regions, as above), given the
 // row's window [lo, top]. Only candidates >= lo count: when they number k or more the row's k-th key is >= lo,
 // and then every position of the row's top-k is a candidate (a chunk keeps all its keys >= lo, or its own exact
 // top-cap when it has more than cap of them). One histogram pass over [lo, top] (kBins bins) finds the bin of
 // the k-th key; the few candidates in that bin are ranked against each other to give the exact threshold T and
 // the number of T-valued keys to take. Returns false, having emitted nothing, when the window does not settle
-// it: fewer than k candidates >= lo, k or more above top, or more than kStreamThreads candidates in the bin;
+// it: fewer than k candidates >= lo, k or more above top, or more than W * 64 candidates in the bin;
 // the caller then selects over the whole row.
 template <class Emit, int W>
 __device__ __forceinline__ bool window_select_emit(const uint32_t (&ccs)[W], uint32_t lo, uint32_t top,
@@ -706,14 +705,14 @@ hipError_t launch_topk_rows(const float *scores, int64_t ld, const int32_t *q_po
 
 // ---------------------------------------------------------------------------------------------------------
 // Windowed chunked form for batches of few rows (decode): each row is split into chunks of `chunk` keys, one
-// 256-thread workgroup per chunk, so the batch fills the chip. Every workgroup of a row takes the same sample of
+// 16-wave workgroup per chunk, so the batch fills the chip. Every workgroup of a row takes the same sample of
 // the row as the streaming form (the runs are read from L2 after the first workgroup) and derives the same lower
-// bound lo of the window that holds the k-th best key. Chunk c keeps its keys >= lo in LDS during one pass (the
-// streaming form's collect step over its four wave segments) and writes them, in position order, with their
+// bound lo of the window that holds the k-th best key. Chunk c keeps its keys >= lo in LDS during one pass (one
+// region per wave, as in the streaming form's collect step) and writes them, in position order, with their
 // count: a few hundred per chunk instead of k. A chunk with more than cap = min(k, chunk) such keys, or more than
 // a wave's LDS region holds, writes its own exact top-cap instead (it contains the row's top-k within that chunk
 // under the same total order; when the chunk's keys >= lo fit cap but not a wave's region, that top-cap also
-// holds keys below lo). The merge pass (one workgroup per row) gathers the row's M candidates into LDS, in
+// holds keys below lo). The merge pass (one 16-wave workgroup per row) gathers the row's M candidates into LDS, in
 // position order, and selects k among those >= lo with one histogram pass over the window (window_select_emit).
 // When k or more candidates are >= lo the selection is exact (the row's k-th best key is then >= lo, so every
 // kept key is a candidate); otherwise the window missed and the merge selects over the whole row from the scores
@@ -916,9 +915,11 @@ size_t topk_windowed_ws_bytes(int num_q, int n_chunks, int cap) {
   return (pairs * 8 + 15) / 16 * 16 + (size_t)num_q * (n_chunks + 2) * 4;   // + counts, + each row's window
 }
 
-template <int V>
-static void launch_wchunk(const float *scores, int64_t ld, const int32_t *q_pos, int num_q, int k, int n_chunks, int cap,
-                          uint32_t *ck, int32_t *cp, uint32_t *cc, hipStream_t s) {
+// One chunk of CHUNK keys per workgroup: V 16-byte loads per lane of kChunkWaves waves.
+template <int CHUNK>
+static void launch_wchunk(const float *scores, int64_t ld, const int32_t *q_pos, int num_q, int k, int n_chunks,
+                          int cap, uint32_t *ck, int32_t *cp, uint32_t *cc, hipStream_t s) {
+  constexpr int V = CHUNK / (4 * kChunkWaves * kWave);
   hipLaunchKernelGGL((topk_wchunk_kernel<V, kChunkWaves>), dim3(num_q, n_chunks), dim3(kChunkWaves * kWave), 0, s,
                      scores, ld, q_pos, k, n_chunks, cap, ck, cp, cc);
 }
@@ -932,9 +933,9 @@ hipError_t launch_topk_windowed(const float *scores, int64_t ld, const int32_t *
   int32_t *cp = reinterpret_cast<int32_t *>(ck + pairs);
   uint32_t *cc = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) + (pairs * 8 + 15) / 16 * 16);
   switch (chunk) {
-    case 4096: launch_wchunk<4096 / (4 * kChunkWaves * kWave)>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
-    case 8192: launch_wchunk<8192 / (4 * kChunkWaves * kWave)>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
-    case 16384: launch_wchunk<16384 / (4 * kChunkWaves * kWave)>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
+    case 4096: launch_wchunk<4096>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
+    case 8192: launch_wchunk<8192>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
+    case 16384: launch_wchunk<16384>(scores, ld, q_pos, num_q, k, n_chunks, cap, ck, cp, cc, s); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
