@@ -7,6 +7,7 @@
 namespace dsa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -105,14 +106,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-// Four OCP E4M3 bytes -> four bf16 (exact: every E4M3 value is a bf16 value), packed as two dwords.
-// The hardware converts to fp32; the fp32 -> bf16 step only drops zero low mantissa bits.
+// Four OCP E4M3 bytes -> four bf16 (exact: every E4M3 value is a bf16 value), packed as two dwords: gfx950's
+// scaled packed convert, two bytes per instruction, with a scale of exactly 1.
 __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t four) {
-  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)four, false);
-  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)four, true);
   u32x2 r;
-  r.x = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u);
-  r.y = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u);
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(four, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(four, 1.0f, true));
   return r;
 }
 
