@@ -308,7 +308,7 @@ __device__ __forceinline__ void stream_window(const float *__restrict__ row, int
 //      keys above hi.
 __device__ __forceinline__ void stream_collect(const float *__restrict__ row, int s0, int s1, bool vec, uint32_t lo,
                                                uint32_t hi, StreamShared &sh, uint32_t &ca, uint32_t &cc) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int w = threadIdx.x / kWave;
   const int cb = w * kCandPerWave;
   ca = 0u;
   cc = 0u;
