@@ -209,21 +209,24 @@ struct PipeCfg {
 // ceil(total / target) up that makes at most `target` chunks in all. Every wave computes the same split from
 // q_pos; false for a workgroup past the last chunk.
 template <int ROWS, int BK>
-__device__ __forceinline__ bool balanced_unit(const IndexerArgs &a, int row_blocks, int target, int u, int &rb,
-                                              int &c, int &bpc) {
-  const int lane = threadIdx.x & 63;
-  auto nblocks = [&](int r) {
-    int p = -1;
+__device__ __forceinline__ int row_block_nblocks(const IndexerArgs &a, int r) {
+  int p = -1;
 #pragma unroll
-    for (int i = 0; i < ROWS; ++i) {
-      const int row = r * ROWS + i;
-      if (row < a.num_q) p = max(p, a.q_pos[row]);
-    }
-    return p < 0 ? 0 : p / BK + 1;
-  };
-  // the block counts of the first 64 row blocks stay in a register (a decode batch rarely has more), so the
-  // passes below pay one load latency, not one each; the wave reductions and scans run on DPP
-  const int nb0 = lane < row_blocks ? nblocks(lane) : 0;
+  for (int i = 0; i < ROWS; ++i) {
+    const int row = r * ROWS + i;
+    if (row < a.num_q) p = max(p, a.q_pos[row]);
+  }
+  return p < 0 ? 0 : p / BK + 1;
+}
+
+// nb0: this lane's row block's block count (row block `lane`; 0 past the last), which the caller loads: the
+// block counts of the first 64 row blocks stay in a register (a decode batch rarely has more), so the passes
+// below pay one load latency, not one each; the wave reductions and scans run on DPP
+template <int ROWS, int BK>
+__device__ __forceinline__ bool balanced_unit(const IndexerArgs &a, int row_blocks, int target, int u, int nb0,
+                                              int &rb, int &c, int &bpc) {
+  const int lane = threadIdx.x & 63;
+  auto nblocks = [&](int r) { return row_block_nblocks<ROWS, BK>(a, r); };
   auto nb_of = [&](int base) {
     const int r = base + lane;
     return base == 0 ? nb0 : (r < row_blocks ? nblocks(r) : 0);
@@ -284,7 +287,8 @@ __global__ __launch_bounds__((NW + 1) * kWave) void indexer_pipe_kernel(IndexerA
   int rb, kb_base, bpc;
   if (balance_target > 0) {
     int c;
-    if (!balanced_unit<ROWS, C::BK>(a, row_blocks, balance_target, (int)blockIdx.x, rb, c, bpc)) return;
+    const int nb0 = lane < row_blocks ? row_block_nblocks<ROWS, C::BK>(a, lane) : 0;
+    if (!balanced_unit<ROWS, C::BK>(a, row_blocks, balance_target, (int)blockIdx.x, nb0, rb, c, bpc)) return;
     rb = __builtin_amdgcn_readfirstlane(rb);   // wave-uniform values: keep them (and the addresses) scalar
     c = __builtin_amdgcn_readfirstlane(c);
     bpc = __builtin_amdgcn_readfirstlane(bpc);
@@ -831,6 +835,277 @@ size_t indexer_topk_ws_bytes(int num_q, int max_kv_len, int k) {
   return (size_t)num_q * n_chunks * k * 8;
 }
 
+// Decode batches (one or two query rows per sequence, H_I = 64, d_I = 128, contiguous caches or pages of at
+// least 32 keys): every wave streams its own run of 32-key tiles from HBM straight into registers, so there is no
+// LDS staging, no producer wave and no workgroup barrier between the loads and the MFMAs. The split is the
+// balanced one above at wave granularity (one unit = one wave, one block = one 32-key tile), and each wave keeps
+// D tiles of loads in flight in a register ring.
+//
+// The arithmetic is the staged kernels' own: for K step s lane (n, g) feeds the MFMA the 8 key elements
+// 16 s + 8 g .. +7 of key n (bf16: bytes 32 s + 16 g .. +15, one 16-byte chunk; FP8: bytes 16 s + 8 g .. +7), the
+// accumulators see the steps in the same order, and the epilogue sums the heads in the same order, so every score
+// is bit-identical to theirs. Loads: for bf16 keys, load j of lane (n, g) is exactly step j's chunk (2 j + g); for
+// FP8 keys, load j of lane (n, g) brings chunk 2 j + g (step 2 j + g, both half-waves' bytes), and one
+// v_permlane32_swap per dword pair hands each half-wave the bytes it needs of steps 2 j and 2 j + 1. Lanes n and
+// n + 32 read 32 adjacent bytes of key n in every load, and a tile's loads cover its 32 key rows whole.
+namespace dk {
+constexpr int HI = 64, DI = 128, MT = 2, KS = 8;
+}
+
+template <bool FP8, int ROWS, int NW, int D, bool PAGED>
+__global__ __launch_bounds__(NW * kWave) void indexer_decode_kernel(IndexerArgs a, int row_blocks, int target) {
+  using namespace dk;
+  constexpr int ROW_BYTES = FP8 ? DI : 2 * DI;
+  constexpr int NLD = ROW_BYTES / 32;   // 16-byte loads per lane per tile
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int n = lane & 31, g = lane >> 5;
+  // positions and sequences of the rows of row block `lane` (the first 64 row blocks): the split's block counts,
+  // and the wave's own rows by a lane read when its row block is among them
+  int qp[ROWS], qs[ROWS];
+  int pmax0 = -1;
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    const int row = lane * ROWS + i;
+    const bool ok = row < a.num_q;
+    qp[i] = ok ? a.q_pos[row] : -1;
+    qs[i] = ok ? a.q_seq[row] : -1;
+    pmax0 = max(pmax0, qp[i]);
+  }
+  int rb, c, bpc;
+  if (!balanced_unit<ROWS, 32>(a, row_blocks, target, (int)blockIdx.x * NW + wv, pmax0 < 0 ? 0 : pmax0 / 32 + 1, rb,
+                               c, bpc))
+    return;
+  rb = __builtin_amdgcn_readfirstlane(rb);
+  c = __builtin_amdgcn_readfirstlane(c);
+  bpc = __builtin_amdgcn_readfirstlane(bpc);
+  const int r0 = rb * ROWS;
+  int rpos[ROWS], rseq[ROWS];
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    const int row = r0 + i;
+    if (rb < kWave) {
+      rpos[i] = __builtin_amdgcn_readlane(qp[i], rb);
+      rseq[i] = __builtin_amdgcn_readlane(qs[i], rb);
+    } else {
+      rpos[i] = row < a.num_q ? a.q_pos[row] : -1;
+      rseq[i] = row < a.num_q ? a.q_seq[row] : -1;
+    }
+  }
+
+  // The row operands (Q fragments, head weights) are loaded after the first tiles' loads have gone out, so the
+  // two latencies overlap; one full wait then covers both, and the tile loop starts with no load of unknown age
+  // in flight (the compiler's waits for the operands would otherwise sit inside the loop and drain the ring).
+  bf16x8 qf[ROWS][MT][KS];
+  float wr[ROWS][MT][16];
+  auto load_rows = [&]() {
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+      const int row = r0 + i;
+      const bool ok = row < a.num_q;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (ok) v = *(const u32x4 *)((const uint16_t *)a.q_idx + ((int64_t)row * HI + t * 32 + n) * DI + s * 16 + g * 8);
+          qf[i][t][s] = __builtin_bit_cast(bf16x8, v);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {   // heads t*32 + 8q + 4g .. +3
+          f32x4 v = {0.f, 0.f, 0.f, 0.f};
+          if (ok) v = *(const f32x4 *)(a.w + (int64_t)row * HI + t * 32 + q * 8 + g * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wr[i][t][q * 4 + e] = v[e];
+        }
+      }
+    }
+  };
+  bool rows_loaded = false;
+
+  const uint8_t *kbase = (const uint8_t *)a.k_idx;
+  const int shift = a.slot.page_shift;
+  int seg = 0;
+  while (seg < ROWS && r0 + seg < a.num_q) {
+    const int b = __builtin_amdgcn_readfirstlane(rseq[seg]);
+    int seg_end = seg + 1;
+    int p_max = rpos[seg];
+    while (seg_end < ROWS && r0 + seg_end < a.num_q && rseq[seg_end] == b) {
+      p_max = max(p_max, rpos[seg_end]);
+      ++seg_end;
+    }
+    p_max = __builtin_amdgcn_readfirstlane(p_max);
+    // score stores go through one buffer resource per row whose size is the row's causal extent in this segment
+    // (zero for a row of another sequence): stores past q_pos are dropped by the hardware, so neither the loop nor
+    // the stores branch, and the compiler can count the loads in flight exactly
+    __amdgpu_buffer_rsrc_t rs[ROWS];
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+      const bool in = i >= seg && i < seg_end;
+      rs[i] = __builtin_amdgcn_make_buffer_rsrc(a.scores + (int64_t)(in ? r0 + i : 0) * a.ld, (short)0,
+                                                in ? (rpos[i] + 1) * 4 : 0, 0x00020000);
+    }
+    const int t_lo = c * bpc;
+    const int nt = min(t_lo + bpc, p_max / 32 + 1) - t_lo;
+    if (nt > 0) {
+      // contiguous: the sequence's rows start at slot b * seq_stride; paged: the page id of the tile a ring slot
+      // loads next is itself loaded one ring turn ahead (a wave-uniform value in a vector register), so the key
+      // loads never wait on a page-table lookup and every load of the loop is unconditional
+      const int64_t seq0 = (int64_t)b * a.slot.seq_stride;
+      const int32_t *ptab = PAGED ? a.slot.page_table + (int64_t)b * a.slot.max_pages : nullptr;
+      auto page_of = [&](int t) { return ptab[min(t * 32, p_max) >> shift]; };
+      const int t_end = t_lo + nt - 1;   // last tile of the run
+
+      u32x4 kd[D][NLD];
+      float sg[D];
+      int pgv[D];
+      // tile t's loads into ring slot j (key s = min(32 t + n, p_max): keys past p_max are never scored), then the
+      // page id of t_next, the tile slot j loads after t
+      auto issue = [&](int t, int t_next, int j) {
+        const int s = min(t * 32 + n, p_max);
+        const uint8_t *rowp;
+        const float *scp;
+        if constexpr (PAGED) {
+          const int64_t slot0 = (int64_t)__builtin_amdgcn_readfirstlane(pgv[j]) << shift;
+          const int off = s & ((1 << shift) - 1);
+          rowp = kbase + slot0 * ROW_BYTES + (uint32_t)(off * ROW_BYTES);
+          scp = FP8 ? a.k_scale + slot0 + off : nullptr;
+        } else {
+          rowp = kbase + seq0 * ROW_BYTES + (uint32_t)(s * ROW_BYTES);
+          scp = FP8 ? a.k_scale + seq0 + s : nullptr;
+        }
+#pragma unroll
+        for (int l = 0; l < NLD; ++l) kd[j][l] = *(const u32x4 *)(rowp + (2 * l + g) * 16);
+        if constexpr (FP8) sg[j] = *scp;
+        if constexpr (PAGED) pgv[j] = page_of(t_next);
+      };
+
+      // lanes n < 32 store key t*32 + n; lanes 32..63 hold the same sums and store past every resource's end (the
+      // whole offset is in the VGPR operand, which the range check covers; 2^31 + 4 * 2^20 stays below 2^32)
+      const uint32_t voff = g ? 0x7ffffff0u : (uint32_t)n * 4u;
+      // Software pipeline: the MFMAs of tile t accumulate into one of two accumulator sets while the epilogue of
+      // tile t - 1 (ReLU, w-weighting, head sum, store) runs on the other, so the VALU work of one tile overlaps
+      // the MFMAs of the next. The set's tile index and scale travel with it (the ring slot is reloaded meanwhile).
+      f32x16 acc[2][ROWS][MT];
+      float sgp[2] = {1.f, 1.f};
+      int tp[2] = {-1, -1};   // tile -1: every store offset lies past the resources' ends (no store)
+#pragma unroll
+      for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[1][i][m] = f32x16{};
+      auto mfmas = [&](int t, int j, int par) {
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acc[par][i][m] = f32x16{};
+#pragma unroll
+        for (int l = 0; l < NLD; ++l) {
+          u32x4 v = kd[j][l];
+          if constexpr (FP8) {
+            // lanes 0..31 take the partner's first dword pair (step 2l + 1, half 0) in place of their second;
+            // lanes 32..63 take the partner's second pair (step 2l, half 1) in place of their first.
+            // v_permlane32_swap swaps lanes 32..63 of its first operand with lanes 0..31 of its second.
+            const auto x = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+            const auto y = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+            v.x = x[0];
+            v.z = x[1];
+            v.y = y[0];
+            v.w = y[1];
+          }
+#pragma unroll
+          for (int h = 0; h < (FP8 ? 2 : 1); ++h) {
+            bf16x8 bfr;
+            if constexpr (FP8) {
+              const u32x2 lo = fp8x4_to_bf16x4(h ? v.z : v.x), hi = fp8x4_to_bf16x4(h ? v.w : v.y);
+              const u32x4 cv = {lo.x, lo.y, hi.x, hi.y};
+              bfr = __builtin_bit_cast(bf16x8, cv);
+            } else {
+              bfr = __builtin_bit_cast(bf16x8, v);
+            }
+            const int s = FP8 ? 2 * l + h : l;
+#pragma unroll
+            for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+              for (int m = 0; m < MT; ++m)
+                acc[par][i][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[i][m][s], bfr, acc[par][i][m], 0, 0, 0);
+          }
+        }
+        sgp[par] = FP8 ? sg[j] : 1.f;
+        tp[par] = t;
+      };
+      auto epilogue = [&](int par) {
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i) {
+          float part = 0.f;
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) part = fmaf(wr[i][m][e], relu(acc[par][i][m][e]), part);
+          part = xor32_sum(part);   // own + other half-wave
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part * sgp[par]), rs[i],
+                                                voff + (uint32_t)tp[par] * 128u, 0, 0);
+        }
+      };
+
+      // Every group of U tiles runs the same straight-line code (the loads of a slot's next tile go out as soon
+      // as its tile is consumed; past the run's end they reload its last tile), so the loads in flight are counted
+      // exactly; the last nt % U tiles follow with their loads already issued. The scheduling fences keep the
+      // compiler from merging consecutive tiles' MFMAs, which would need several tiles' keys at once.
+      constexpr int U = D % 2 ? 2 * D : D;   // a whole number of ring turns and of accumulator-set turns
+      if constexpr (PAGED) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) pgv[j] = page_of(min(t_lo + j, t_end));
+      }
+#pragma unroll
+      for (int j = 0; j < D; ++j) issue(min(t_lo + j, t_end), min(t_lo + j + D, t_end), j);
+      if (!rows_loaded) {
+        load_rows();
+        rows_loaded = true;
+      }
+      wait_vmcnt<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      int i0 = 0;
+      for (; i0 + U <= nt; i0 += U) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          mfmas(t_lo + i0 + k, k % D, k % 2);
+          epilogue((k + 1) % 2);
+          __builtin_amdgcn_sched_barrier(0);
+          issue(min(t_lo + i0 + k + D, t_end), min(t_lo + i0 + k + 2 * D, t_end), k % D);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < U - 1; ++k) {
+        if (i0 + k < nt) {
+          mfmas(t_lo + i0 + k, k % D, k % 2);
+          epilogue((k + 1) % 2);
+          if (k + D < U - 1 && i0 + k + D < nt)   // a tile of this tail whose slot is not yet loaded
+            issue(t_lo + i0 + k + D, t_lo + i0 + k + D, k % D);
+        }
+      }
+      // the last tile's epilogue (tile i of the run used set i % 2)
+      if ((nt - 1) % 2) epilogue(1); else epilogue(0);
+    }
+    seg = seg_end;
+  }
+}
+
+template <bool FP8, int ROWS, int NW, int D>
+static hipError_t launch_decode(const IndexerArgs &a, int target_waves, hipStream_t st) {
+  const int row_blocks = (a.num_q + ROWS - 1) / ROWS;
+  // the split makes at most max(target, row_blocks) chunks (one per row block when even that exceeds the target)
+  const int units = max(target_waves, row_blocks);
+  const dim3 grid((units + NW - 1) / NW);
+  if (a.slot.page_table != nullptr)
+    hipLaunchKernelGGL((indexer_decode_kernel<FP8, ROWS, NW, D, true>), grid, dim3(NW * kWave), 0, st, a, row_blocks,
+                       target_waves);
+  else
+    hipLaunchKernelGGL((indexer_decode_kernel<FP8, ROWS, NW, D, false>), grid, dim3(NW * kWave), 0, st, a, row_blocks,
+                       target_waves);
+  return hipGetLastError();
+}
+
 // Key-range chunks per row block: enough workgroups to fill the chip when rows are few.
 struct Split {
   int chunks, bpc;   // chunks of the key range, key blocks per chunk
@@ -854,6 +1129,15 @@ static hipError_t launch_t(const IndexerArgs &a, int target_wgs, hipStream_t st)
       hipLaunchKernelGGL(indexer_prefill_kernel, dim3(row_blocks, sp.chunks), dim3(pf::WAVES * kWave), 0, st, a,
                          sp.bpc, row_blocks);
       return hipGetLastError();
+    }
+  }
+  if constexpr (HI == dk::HI && DI == dk::DI && ROWS < 8) {
+    // decode batches: register-streamed tiles, one wave per unit of the balanced split
+    if (a.slot.page_table == nullptr || a.slot.page_shift >= 5) {
+      // one row a wave: two waves a SIMD, three FP8 (two bf16) tiles in the ring; two rows a wave (their Q, w and
+      // two accumulator sets): one wave a SIMD, two tiles in the ring (deeper rings spill)
+      if constexpr (ROWS == 1) return launch_decode<FP8, 1, 8, FP8 ? 3 : 2>(a, target_wgs * 8, st);
+      else return launch_decode<FP8, ROWS, 4, 2>(a, target_wgs * 4, st);
     }
   }
   const Split sp = key_split(a.max_kv_len, C::BK, row_blocks, target_wgs);
