@@ -115,8 +115,9 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t four) {
   return r;
 }
 
-// Value of lane l ^ 32 (the other half-wave), via gfx950's v_permlane32_swap: with both operands equal, the
-// swap leaves (partner, own) in lanes 0..31 and (own, partner) in lanes 32..63.
+// Value of lane l ^ 32 (the other half-wave), via gfx950's v_permlane32_swap, which swaps lanes 32..63 of its first
+// operand with lanes 0..31 of its second: with both operands equal it leaves (own, partner) in lanes 0..31 and
+// (partner, own) in lanes 32..63, so the sum and the max below are the same in both halves.
 __device__ __forceinline__ float xor32_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
   return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
