@@ -681,165 +681,12 @@ void indexer_prefill_kernel(IndexerArgs a, int blocks_per_chunk, int row_blocks)
   }
 }
 
-// Fused indexer -> top-k for decode batches: a workgroup scores one 8192-key chunk of one query row into LDS and
-// selects the chunk's top-k there, so the scores never reach HBM; topk_merge_kernel then selects among the
-// chunks' candidates. The "Sparse Attention Architecture Evolution" page names fusing the indexer operators as
-// the deployment optimisation; the scoring arithmetic (MFMA order, head-sum order, sigma after the sum) is the
-// decode indexer's, so the selection is the one dsa_topk makes from dsa_indexer_scores' output for such batches.
-// Eight waves stage 256-key (FP8) or 128-key (bf16) tiles through LDS with global->LDS loads, three in flight, and
-// each scores 32-key groups; the select is the shared block-wide bucket select over 16 keys per thread.
-namespace ft {
-constexpr int WAVES = 8, NT = WAVES * kWave;
-constexpr int KC = 8192;                       // keys of one workgroup
-constexpr int HI = 64, DI = 128, MT = 2, KS = 8;
-constexpr int TILE = 32768, NBUF = 3;
-constexpr int LPW = TILE / (kWave * 16) / WAVES;   // 1 KB loads per wave per tile
-constexpr int ITEMS = KC / NT;
-template <bool FP8>
-struct Cfg {
-  static constexpr int ROW_BYTES = FP8 ? DI : 2 * DI;
-  static constexpr int CPK = ROW_BYTES / 16;
-  static constexpr int BK = TILE / ROW_BYTES;     // keys per tile
-  static constexpr int GROUPS = BK / 32;
-  static constexpr int RPL = kWave / CPK;         // key rows per load
-  __device__ static __forceinline__ int swz(int chunk, int kk) { return chunk ^ (kk & (CPK - 1)); }
-};
-}  // namespace ft
 
-template <bool FP8>
-__global__ __launch_bounds__(ft::NT) void indexer_topk_kernel(IndexerArgs a, int k, int n_chunks,
-                                                              uint32_t *__restrict__ cand_key,
-                                                              int32_t *__restrict__ cand_pos) {
-  using namespace ft;
-  using C = Cfg<FP8>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[NBUF * TILE];
-  __shared__ float sc[KC];
-  __shared__ TopkSharedT<NT> tsh;
-
-  const int r = blockIdx.x, c = blockIdx.y;
-  const int b = a.q_seq[r], p = a.q_pos[r], n = p + 1;
-  if (n <= k) return;                 // the merge pass writes such rows directly
-  const int start = c * KC;
-  if (start >= n) return;
-  const int len = min(KC, n - start);
-  const int nt = (len + C::BK - 1) / C::BK;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nn = lane & 31, g = lane >> 5;
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds_k;
-
-  bf16x8 qf[MT][KS];
-  float wr[MT][16];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int head = t * 32 + nn;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qf[t][s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)((const uint16_t *)a.q_idx + ((int64_t)r * HI + head) * DI +
-                                                             s * 16 + g * 8));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) wr[t][i] = a.w[(int64_t)r * HI + t * 32 + (i >> 2) * 8 + g * 4 + (i & 3)];
-  }
-  wait_vmcnt<0>();   // row operands in registers before the tile loads are counted
-
-  // wave wv loads rows of its LPW loads of tile kb; keys past p load key p (in the cache, never scored)
-  const int q_ld = lane / C::CPK, pc = lane % C::CPK;
-  auto issue = [&](int kb) {
-    const uint32_t dst = lds_base + (uint32_t)((kb % NBUF) * TILE);
-#pragma unroll
-    for (int jj = 0; jj < LPW; ++jj) {
-      const int j = wv * LPW + jj;
-      const int kk = j * C::RPL + q_ld;
-      const int s = min(start + kb * C::BK + kk, p);
-      const uint64_t src = (uint64_t)((const uint8_t *)a.k_idx + a.slot(b, s) * C::ROW_BYTES + C::swz(pc, kk) * 16);
-      load_lds_16(src, dst + (uint32_t)(j * kWave * 16));
-    }
-  };
-  issue(0);
-  if (nt > 1) issue(1);
-  if (nt > 2) issue(2);
-  for (int kb = 0; kb < nt; ++kb) {
-    // tile kb has landed once at most the later tiles' loads are outstanding (loads complete in order)
-    const int later = min(nt - 1 - kb, 2);
-    if (later == 2) wait_vmcnt<2 * LPW>(); else if (later == 1) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
-    lds_barrier();
-    const uint8_t *tile = lds_k + (kb % NBUF) * TILE;
-    for (int grp = wv; grp < C::GROUPS; grp += WAVES) {
-      const int s0 = kb * C::BK + grp * 32;          // relative to start
-      if (start + s0 > p) break;                     // wave-uniform
-      const int kk = grp * 32 + nn;
-      const uint8_t *krow = tile + kk * C::ROW_BYTES;
-      f32x16 acc[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        bf16x8 bfr;
-        if constexpr (FP8) {
-          const u32x2 raw = *(const u32x2 *)(krow + C::swz(s, kk) * 16 + g * 8);
-          const u32x2 lo = fp8x4_to_bf16x4(raw.x), hi = fp8x4_to_bf16x4(raw.y);
-          const u32x4 v = {lo.x, lo.y, hi.x, hi.y};
-          bfr = __builtin_bit_cast(bf16x8, v);
-        } else {
-          bfr = __builtin_bit_cast(bf16x8, *(const u32x4 *)(krow + C::swz(2 * s + g, kk) * 16));
-        }
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][s], bfr, acc[t], 0, 0, 0);
-      }
-      float part = 0.f;
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) part = fmaf(wr[t][i], relu(acc[t][i]), part);
-      part = xor32_sum(part);   // own + other half-wave (v_permlane32_swap)
-      const int sk = start + s0 + nn;
-      if (g == 0 && sk <= p) {
-        if constexpr (FP8) part *= a.k_scale[a.slot(b, sk)];
-        sc[s0 + nn] = part;
-      }
-    }
-    lds_barrier();   // every wave is done with tile kb (and its scores are in LDS)
-    if (kb + 3 < nt) issue(kb + 3);
-  }
-  __syncthreads();
-  uint32_t key[ITEMS];
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int L = i * NT + tid;
-    key[i] = L < len ? order_key(sc[L]) : 0u;
-  }
-  const int64_t dst = ((int64_t)r * n_chunks + c) * k;
-  select_topk<ITEMS, NT>(key, len, k, [&](int rank, int L, uint32_t kv) {
-    cand_key[dst + rank] = kv;
-    cand_pos[dst + rank] = start + L;
-  }, tsh);
-}
-
-hipError_t launch_indexer_topk(const IndexerArgs &a, int k, uint32_t *cand_key, int32_t *cand_pos, int32_t *idx,
-                               hipStream_t st) {
-  if (a.H_I != ft::HI || a.d_I != ft::DI) return hipErrorInvalidValue;
-  const int n_chunks = (a.max_kv_len + ft::KC - 1) / ft::KC;
-  if (a.fp8)
-    hipLaunchKernelGGL(indexer_topk_kernel<true>, dim3(a.num_q, n_chunks), dim3(ft::NT), 0, st, a, k, n_chunks,
-                       cand_key, cand_pos);
-  else
-    hipLaunchKernelGGL(indexer_topk_kernel<false>, dim3(a.num_q, n_chunks), dim3(ft::NT), 0, st, a, k, n_chunks,
-                       cand_key, cand_pos);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_topk_merge(a.q_pos, a.num_q, k, ft::KC, n_chunks, cand_key, cand_pos, idx, st);
-}
-
-size_t indexer_topk_ws_bytes(int num_q, int max_kv_len, int k) {
-  const int n_chunks = (max_kv_len + ft::KC - 1) / ft::KC;
-  return (size_t)num_q * n_chunks * k * 8;
-}
-
-// Decode batches (one or two query rows per sequence, H_I = 64, d_I = 128, contiguous caches or pages of at
-// least 32 keys): every wave streams its own run of 32-key tiles from HBM straight into registers, so there is no
-// LDS staging, no producer wave and no workgroup barrier between the loads and the MFMAs. The split is the
-// balanced one above at wave granularity (one unit = one wave, one block = one 32-key tile), and each wave keeps
-// D tiles of loads in flight in a register ring.
+// Decode batches (one or two query rows per sequence, H_I = 64, d_I = 128, contiguous or paged caches): every wave
+// streams its own run of 32-key tiles from HBM straight into registers, so there is no LDS staging, no producer
+// wave and no workgroup barrier between the loads and the MFMAs. The split is the balanced one above at wave
+// granularity (one unit = one wave, one block = one 32-key tile), and each wave keeps D tiles of loads in flight
+// in a register ring.
 //
 // The arithmetic is the staged kernels' own: for K step s lane (n, g) feeds the MFMA the 8 key elements
 // 16 s + 8 g .. +7 of key n (bf16: bytes 32 s + 16 g .. +15, one 16-byte chunk; FP8: bytes 16 s + 8 g .. +7), the
@@ -852,11 +699,164 @@ namespace dk {
 constexpr int HI = 64, DI = 128, MT = 2, KS = 8;
 }
 
-template <bool FP8, int ROWS, int NW, int D, bool PAGED>
-__global__ __launch_bounds__(NW * kWave) void indexer_decode_kernel(IndexerArgs a, int row_blocks, int target) {
+// One wave's run of 32-key tiles t_lo .. t_lo + nt - 1 of sequence b (keys past p_max load key p_max and are
+// never scored) through the MFMAs and epilogues of ROWS rows (Q fragments qf, head weights wr). `operands()` runs
+// once the first ring turn of loads is out (a caller loads the rows' Q and w there), and every load has landed
+// before the first tile is consumed. emit(t, i, v) receives row i's score v of key 32 t + n in lane (n, g) (both
+// half-waves hold it); t = -1 means no tile (the pipeline's start), with nothing to store.
+//
+// Loads: a ring of D tiles, refilled as soon as a tile is consumed; past the run's end it reloads the last tile,
+// so every group of U tiles runs the same straight-line code and the compiler counts the loads in flight exactly
+// (the last nt % U tiles follow with their loads already issued). PM = 0: a contiguous cache, the sequence starting
+// at slot b * seq_stride. PM = 1 (pages of at least 32 keys, so a tile lies in one page) and PM = 2 (shorter pages):
+// the page id (PM = 1: the tile's, one value for the wave; PM = 2: each lane's key's) of the tile a ring slot loads
+// next is loaded one ring turn ahead, so the key loads never wait on a page-table lookup. The scheduling fences
+// keep the compiler from merging consecutive tiles' MFMAs, which would need several tiles' keys at once.
+//
+// Software pipeline: the MFMAs of tile t accumulate into one of two accumulator sets while the epilogue of tile
+// t - 1 (ReLU, w-weighting, head sum) runs on the other, so the VALU work of one tile overlaps the MFMAs of the
+// next; the set's tile index and scale travel with it (the ring slot is reloaded meanwhile).
+template <bool FP8, int ROWS, int D, int PM, class Operands, class Emit>
+__device__ __forceinline__ void stream_key_tiles(const IndexerArgs &a, int b, int p_max, int t_lo, int nt,
+                                                 const bf16x8 (&qf)[ROWS][dk::MT][dk::KS],
+                                                 const float (&wr)[ROWS][dk::MT][16], Operands operands, Emit emit) {
   using namespace dk;
   constexpr int ROW_BYTES = FP8 ? DI : 2 * DI;
   constexpr int NLD = ROW_BYTES / 32;   // 16-byte loads per lane per tile
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31, g = lane >> 5;
+  const uint8_t *kbase = (const uint8_t *)a.k_idx;
+  const int shift = a.slot.page_shift;
+  const int64_t seq0 = (int64_t)b * a.slot.seq_stride;
+  const int32_t *ptab = PM ? a.slot.page_table + (int64_t)b * a.slot.max_pages : nullptr;
+  auto page_of = [&](int t) {   // the tile's page (PM = 1) or this lane's key's (PM = 2)
+    return ptab[min(t * 32 + (PM == 2 ? n : 0), p_max) >> shift];
+  };
+  const int t_end = t_lo + nt - 1;   // last tile of the run
+
+  u32x4 kd[D][NLD];
+  float sg[D];
+  int pgv[D];
+  // tile t's loads into ring slot j (key s = min(32 t + n, p_max)), then the page ids of t_next, the tile slot j
+  // loads after t
+  auto issue = [&](int t, int t_next, int j) {
+    const int s = min(t * 32 + n, p_max);
+    const uint8_t *rowp;
+    const float *scp;
+    if constexpr (PM == 2) {
+      const int64_t slot = ((int64_t)pgv[j] << shift) + (s & ((1 << shift) - 1));
+      rowp = kbase + slot * ROW_BYTES;
+      scp = FP8 ? a.k_scale + slot : nullptr;
+    } else {
+      // one base per tile for the wave (scalar), the key's offset from it in 32 bits
+      const int64_t slot0 = PM ? (int64_t)__builtin_amdgcn_readfirstlane(pgv[j]) << shift : seq0;
+      const int off = PM ? (s & ((1 << shift) - 1)) : s;
+      rowp = kbase + slot0 * ROW_BYTES + (uint32_t)(off * ROW_BYTES);
+      scp = FP8 ? a.k_scale + slot0 + off : nullptr;
+    }
+#pragma unroll
+    for (int l = 0; l < NLD; ++l) kd[j][l] = *(const u32x4 *)(rowp + (2 * l + g) * 16);
+    if constexpr (FP8) sg[j] = *scp;
+    if constexpr (PM != 0) pgv[j] = page_of(t_next);
+  };
+
+  f32x16 acc[2][ROWS][MT];
+  float sgp[2] = {1.f, 1.f};
+  int tp[2] = {-1, -1};
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[1][i][m] = f32x16{};
+  auto mfmas = [&](int t, int j, int par) {
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[par][i][m] = f32x16{};
+#pragma unroll
+    for (int l = 0; l < NLD; ++l) {
+      u32x4 v = kd[j][l];
+      if constexpr (FP8) {
+        // lanes 0..31 take the partner's first dword pair (step 2l + 1, half 0) in place of their second;
+        // lanes 32..63 take the partner's second pair (step 2l, half 1) in place of their first.
+        // v_permlane32_swap swaps lanes 32..63 of its first operand with lanes 0..31 of its second.
+        const auto x = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+        const auto y = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+        v.x = x[0];
+        v.z = x[1];
+        v.y = y[0];
+        v.w = y[1];
+      }
+#pragma unroll
+      for (int h = 0; h < (FP8 ? 2 : 1); ++h) {
+        bf16x8 bfr;
+        if constexpr (FP8) {
+          const u32x2 lo = fp8x4_to_bf16x4(h ? v.z : v.x), hi = fp8x4_to_bf16x4(h ? v.w : v.y);
+          const u32x4 cv = {lo.x, lo.y, hi.x, hi.y};
+          bfr = __builtin_bit_cast(bf16x8, cv);
+        } else {
+          bfr = __builtin_bit_cast(bf16x8, v);
+        }
+        const int s = FP8 ? 2 * l + h : l;
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            acc[par][i][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[i][m][s], bfr, acc[par][i][m], 0, 0, 0);
+      }
+    }
+    sgp[par] = FP8 ? sg[j] : 1.f;
+    tp[par] = t;
+  };
+  auto epilogue = [&](int par) {
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+      float part = 0.f;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) part = fmaf(wr[i][m][e], relu(acc[par][i][m][e]), part);
+      part = xor32_sum(part);   // own + other half-wave
+      emit(tp[par], i, part * sgp[par]);
+    }
+  };
+
+  constexpr int U = D % 2 ? 2 * D : D;   // a whole number of ring turns and of accumulator-set turns
+  if constexpr (PM != 0) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) pgv[j] = page_of(min(t_lo + j, t_end));
+  }
+#pragma unroll
+  for (int j = 0; j < D; ++j) issue(min(t_lo + j, t_end), min(t_lo + j + D, t_end), j);
+  operands();
+  wait_vmcnt<0>();
+  __builtin_amdgcn_sched_barrier(0);
+  int i0 = 0;
+  for (; i0 + U <= nt; i0 += U) {
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      mfmas(t_lo + i0 + k, k % D, k % 2);
+      epilogue((k + 1) % 2);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(min(t_lo + i0 + k + D, t_end), min(t_lo + i0 + k + 2 * D, t_end), k % D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < U - 1; ++k) {
+    if (i0 + k < nt) {
+      mfmas(t_lo + i0 + k, k % D, k % 2);
+      epilogue((k + 1) % 2);
+      if (k + D < U - 1 && i0 + k + D < nt)   // a tile of this tail whose slot is not yet loaded
+        issue(t_lo + i0 + k + D, t_lo + i0 + k + D, k % D);
+    }
+  }
+  // the last tile's epilogue (tile i of the run used set i % 2)
+  if ((nt - 1) % 2) epilogue(1); else epilogue(0);
+}
+
+template <bool FP8, int ROWS, int NW, int D, int PM>
+__global__ __launch_bounds__(NW * kWave) void indexer_decode_kernel(IndexerArgs a, int row_blocks, int target) {
+  using namespace dk;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int n = lane & 31, g = lane >> 5;
@@ -923,8 +923,6 @@ __global__ __launch_bounds__(NW * kWave) void indexer_decode_kernel(IndexerArgs 
   };
   bool rows_loaded = false;
 
-  const uint8_t *kbase = (const uint8_t *)a.k_idx;
-  const int shift = a.slot.page_shift;
   int seg = 0;
   while (seg < ROWS && r0 + seg < a.num_q) {
     const int b = __builtin_amdgcn_readfirstlane(rseq[seg]);
@@ -948,147 +946,29 @@ __global__ __launch_bounds__(NW * kWave) void indexer_decode_kernel(IndexerArgs 
     const int t_lo = c * bpc;
     const int nt = min(t_lo + bpc, p_max / 32 + 1) - t_lo;
     if (nt > 0) {
-      // contiguous: the sequence's rows start at slot b * seq_stride; paged: the page id of the tile a ring slot
-      // loads next is itself loaded one ring turn ahead (a wave-uniform value in a vector register), so the key
-      // loads never wait on a page-table lookup and every load of the loop is unconditional
-      const int64_t seq0 = (int64_t)b * a.slot.seq_stride;
-      const int32_t *ptab = PAGED ? a.slot.page_table + (int64_t)b * a.slot.max_pages : nullptr;
-      auto page_of = [&](int t) { return ptab[min(t * 32, p_max) >> shift]; };
-      const int t_end = t_lo + nt - 1;   // last tile of the run
-
-      u32x4 kd[D][NLD];
-      float sg[D];
-      int pgv[D];
-      // tile t's loads into ring slot j (key s = min(32 t + n, p_max): keys past p_max are never scored), then the
-      // page id of t_next, the tile slot j loads after t
-      auto issue = [&](int t, int t_next, int j) {
-        const int s = min(t * 32 + n, p_max);
-        const uint8_t *rowp;
-        const float *scp;
-        if constexpr (PAGED) {
-          const int64_t slot0 = (int64_t)__builtin_amdgcn_readfirstlane(pgv[j]) << shift;
-          const int off = s & ((1 << shift) - 1);
-          rowp = kbase + slot0 * ROW_BYTES + (uint32_t)(off * ROW_BYTES);
-          scp = FP8 ? a.k_scale + slot0 + off : nullptr;
-        } else {
-          rowp = kbase + seq0 * ROW_BYTES + (uint32_t)(s * ROW_BYTES);
-          scp = FP8 ? a.k_scale + seq0 + s : nullptr;
-        }
-#pragma unroll
-        for (int l = 0; l < NLD; ++l) kd[j][l] = *(const u32x4 *)(rowp + (2 * l + g) * 16);
-        if constexpr (FP8) sg[j] = *scp;
-        if constexpr (PAGED) pgv[j] = page_of(t_next);
-      };
-
       // lanes n < 32 store key t*32 + n; lanes 32..63 hold the same sums and store past every resource's end (the
-      // whole offset is in the VGPR operand, which the range check covers; 2^31 + 4 * 2^20 stays below 2^32)
+      // whole offset is in the VGPR operand, which the range check covers; 2^31 + 4 * 2^20 stays below 2^32); tile
+      // -1 stores past every end too
       const uint32_t voff = g ? 0x7ffffff0u : (uint32_t)n * 4u;
-      // Software pipeline: the MFMAs of tile t accumulate into one of two accumulator sets while the epilogue of
-      // tile t - 1 (ReLU, w-weighting, head sum, store) runs on the other, so the VALU work of one tile overlaps
-      // the MFMAs of the next. The set's tile index and scale travel with it (the ring slot is reloaded meanwhile).
-      f32x16 acc[2][ROWS][MT];
-      float sgp[2] = {1.f, 1.f};
-      int tp[2] = {-1, -1};   // tile -1: every store offset lies past the resources' ends (no store)
-#pragma unroll
-      for (int i = 0; i < ROWS; ++i)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[1][i][m] = f32x16{};
-      auto mfmas = [&](int t, int j, int par) {
-#pragma unroll
-        for (int i = 0; i < ROWS; ++i)
-#pragma unroll
-          for (int m = 0; m < MT; ++m) acc[par][i][m] = f32x16{};
-#pragma unroll
-        for (int l = 0; l < NLD; ++l) {
-          u32x4 v = kd[j][l];
-          if constexpr (FP8) {
-            // lanes 0..31 take the partner's first dword pair (step 2l + 1, half 0) in place of their second;
-            // lanes 32..63 take the partner's second pair (step 2l, half 1) in place of their first.
-            // v_permlane32_swap swaps lanes 32..63 of its first operand with lanes 0..31 of its second.
-            const auto x = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
-            const auto y = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
-            v.x = x[0];
-            v.z = x[1];
-            v.y = y[0];
-            v.w = y[1];
-          }
-#pragma unroll
-          for (int h = 0; h < (FP8 ? 2 : 1); ++h) {
-            bf16x8 bfr;
-            if constexpr (FP8) {
-              const u32x2 lo = fp8x4_to_bf16x4(h ? v.z : v.x), hi = fp8x4_to_bf16x4(h ? v.w : v.y);
-              const u32x4 cv = {lo.x, lo.y, hi.x, hi.y};
-              bfr = __builtin_bit_cast(bf16x8, cv);
-            } else {
-              bfr = __builtin_bit_cast(bf16x8, v);
+      stream_key_tiles<FP8, ROWS, D, PM>(
+          a, b, p_max, t_lo, nt, qf, wr,
+          [&]() {
+            if (!rows_loaded) {
+              load_rows();
+              rows_loaded = true;
             }
-            const int s = FP8 ? 2 * l + h : l;
-#pragma unroll
-            for (int i = 0; i < ROWS; ++i)
-#pragma unroll
-              for (int m = 0; m < MT; ++m)
-                acc[par][i][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[i][m][s], bfr, acc[par][i][m], 0, 0, 0);
-          }
-        }
-        sgp[par] = FP8 ? sg[j] : 1.f;
-        tp[par] = t;
-      };
-      auto epilogue = [&](int par) {
-#pragma unroll
-        for (int i = 0; i < ROWS; ++i) {
-          float part = 0.f;
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) part = fmaf(wr[i][m][e], relu(acc[par][i][m][e]), part);
-          part = xor32_sum(part);   // own + other half-wave
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part * sgp[par]), rs[i],
-                                                voff + (uint32_t)tp[par] * 128u, 0, 0);
-        }
-      };
-
-      // Every group of U tiles runs the same straight-line code (the loads of a slot's next tile go out as soon
-      // as its tile is consumed; past the run's end they reload its last tile), so the loads in flight are counted
-      // exactly; the last nt % U tiles follow with their loads already issued. The scheduling fences keep the
-      // compiler from merging consecutive tiles' MFMAs, which would need several tiles' keys at once.
-      constexpr int U = D % 2 ? 2 * D : D;   // a whole number of ring turns and of accumulator-set turns
-      if constexpr (PAGED) {
-#pragma unroll
-        for (int j = 0; j < D; ++j) pgv[j] = page_of(min(t_lo + j, t_end));
-      }
-#pragma unroll
-      for (int j = 0; j < D; ++j) issue(min(t_lo + j, t_end), min(t_lo + j + D, t_end), j);
-      if (!rows_loaded) {
-        load_rows();
-        rows_loaded = true;
-      }
-      wait_vmcnt<0>();
-      __builtin_amdgcn_sched_barrier(0);
-      int i0 = 0;
-      for (; i0 + U <= nt; i0 += U) {
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-          mfmas(t_lo + i0 + k, k % D, k % 2);
-          epilogue((k + 1) % 2);
-          __builtin_amdgcn_sched_barrier(0);
-          issue(min(t_lo + i0 + k + D, t_end), min(t_lo + i0 + k + 2 * D, t_end), k % D);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < U - 1; ++k) {
-        if (i0 + k < nt) {
-          mfmas(t_lo + i0 + k, k % D, k % 2);
-          epilogue((k + 1) % 2);
-          if (k + D < U - 1 && i0 + k + D < nt)   // a tile of this tail whose slot is not yet loaded
-            issue(t_lo + i0 + k + D, t_lo + i0 + k + D, k % D);
-        }
-      }
-      // the last tile's epilogue (tile i of the run used set i % 2)
-      if ((nt - 1) % 2) epilogue(1); else epilogue(0);
+          },
+          [&](int t, int i, float v) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs[i], voff + (uint32_t)t * 128u, 0, 0);
+          });
     }
     seg = seg_end;
   }
+}
+
+// Page mode of stream_key_tiles: 0 contiguous, 1 pages of at least one 32-key tile, 2 shorter pages.
+static int page_mode(const IndexerArgs &a) {
+  return a.slot.page_table == nullptr ? 0 : (a.slot.page_shift >= 5 ? 1 : 2);
 }
 
 template <bool FP8, int ROWS, int NW, int D>
@@ -1096,14 +976,112 @@ static hipError_t launch_decode(const IndexerArgs &a, int target_waves, hipStrea
   const int row_blocks = (a.num_q + ROWS - 1) / ROWS;
   // the split makes at most max(target, row_blocks) chunks (one per row block when even that exceeds the target)
   const int units = max(target_waves, row_blocks);
-  const dim3 grid((units + NW - 1) / NW);
-  if (a.slot.page_table != nullptr)
-    hipLaunchKernelGGL((indexer_decode_kernel<FP8, ROWS, NW, D, true>), grid, dim3(NW * kWave), 0, st, a, row_blocks,
-                       target_waves);
-  else
-    hipLaunchKernelGGL((indexer_decode_kernel<FP8, ROWS, NW, D, false>), grid, dim3(NW * kWave), 0, st, a, row_blocks,
-                       target_waves);
+  const dim3 grid((units + NW - 1) / NW), block(NW * kWave);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, st, a, row_blocks, target_waves); };
+  switch (page_mode(a)) {
+    case 0: go(indexer_decode_kernel<FP8, ROWS, NW, D, 0>); break;
+    case 1: go(indexer_decode_kernel<FP8, ROWS, NW, D, 1>); break;
+    default: go(indexer_decode_kernel<FP8, ROWS, NW, D, 2>); break;
+  }
   return hipGetLastError();
+}
+
+// Fused indexer -> top-k for decode batches: a workgroup scores one 8192-key chunk of one query row into LDS and
+// selects the chunk's top-k there, so the scores never reach HBM; topk_merge_kernel then selects among the
+// chunks' candidates. The "Sparse Attention Architecture Evolution" page names fusing the indexer operators as
+// the deployment optimisation. Each of the eight waves streams 32 of the chunk's 32-key tiles through registers
+// with the decode indexer's own loop (stream_key_tiles), so every score is bit-identical to dsa_indexer_scores'
+// for such batches and the selection is the one dsa_topk makes from it; the select is the shared block-wide bucket
+// select over 16 keys per thread.
+namespace ft {
+constexpr int WAVES = 8, NT = WAVES * kWave;
+constexpr int KC = 8192;                       // keys of one workgroup
+constexpr int TPW = KC / 32 / WAVES;           // 32-key tiles per wave
+constexpr int ITEMS = KC / NT;
+}  // namespace ft
+
+template <bool FP8, int PM>
+__global__ __launch_bounds__(ft::NT) void indexer_topk_kernel(IndexerArgs a, int k, int n_chunks,
+                                                              uint32_t *__restrict__ cand_key,
+                                                              int32_t *__restrict__ cand_pos) {
+  using namespace ft;
+  using dk::MT;
+  using dk::KS;
+  __shared__ float sc[KC];
+  __shared__ TopkSharedT<NT> tsh;
+
+  const int r = blockIdx.x, c = blockIdx.y;
+  const int b = a.q_seq[r], p = a.q_pos[r], n = p + 1;
+  if (n <= k) return;                 // the merge pass writes such rows directly
+  const int start = c * KC;
+  if (start >= n) return;
+  const int len = min(KC, n - start);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nn = lane & 31, g = lane >> 5;
+  const int t_lo = start / 32 + wv * TPW;
+  const int nt = min(TPW, p / 32 + 1 - t_lo);
+  if (nt > 0) {
+    bf16x8 qf[1][MT][KS];
+    float wr[1][MT][16];
+    auto load_row = [&]() {
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          qf[0][t][s] = __builtin_bit_cast(
+              bf16x8, *(const u32x4 *)((const uint16_t *)a.q_idx + ((int64_t)r * dk::HI + t * 32 + nn) * dk::DI +
+                                       s * 16 + g * 8));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {   // heads t*32 + 8q + 4g .. +3
+          const f32x4 v = *(const f32x4 *)(a.w + (int64_t)r * dk::HI + t * 32 + q * 8 + g * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wr[0][t][q * 4 + e] = v[e];
+        }
+      }
+    };
+    // scores of this chunk's keys 0 .. len-1 into LDS (tile -1 is the pipeline's start: nothing to store)
+    stream_key_tiles<FP8, 1, FP8 ? 3 : 2, PM>(a, b, p, t_lo, nt, qf, wr, load_row, [&](int t, int, float v) {
+      const int s = t * 32 + nn;
+      if (t >= 0 && g == 0 && s <= p) sc[s - start] = v;
+    });
+  }
+  __syncthreads();
+  uint32_t key[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int L = i * NT + tid;
+    key[i] = L < len ? order_key(sc[L]) : 0u;
+  }
+  const int64_t dst = ((int64_t)r * n_chunks + c) * k;
+  select_topk<ITEMS, NT>(key, len, k, [&](int rank, int L, uint32_t kv) {
+    cand_key[dst + rank] = kv;
+    cand_pos[dst + rank] = start + L;
+  }, tsh);
+}
+
+hipError_t launch_indexer_topk(const IndexerArgs &a, int k, uint32_t *cand_key, int32_t *cand_pos, int32_t *idx,
+                               hipStream_t st) {
+  if (a.H_I != dk::HI || a.d_I != dk::DI) return hipErrorInvalidValue;
+  const int n_chunks = (a.max_kv_len + ft::KC - 1) / ft::KC;
+  const dim3 grid(a.num_q, n_chunks), block(ft::NT);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, st, a, k, n_chunks, cand_key, cand_pos); };
+  switch (page_mode(a) + (a.fp8 ? 3 : 0)) {
+    case 0: go(indexer_topk_kernel<false, 0>); break;
+    case 1: go(indexer_topk_kernel<false, 1>); break;
+    case 2: go(indexer_topk_kernel<false, 2>); break;
+    case 3: go(indexer_topk_kernel<true, 0>); break;
+    case 4: go(indexer_topk_kernel<true, 1>); break;
+    default: go(indexer_topk_kernel<true, 2>); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topk_merge(a.q_pos, a.num_q, k, ft::KC, n_chunks, cand_key, cand_pos, idx, st);
+}
+
+size_t indexer_topk_ws_bytes(int num_q, int max_kv_len, int k) {
+  const int n_chunks = (max_kv_len + ft::KC - 1) / ft::KC;
+  return (size_t)num_q * n_chunks * k * 8;
 }
 
 // Key-range chunks per row block: enough workgroups to fill the chip when rows are few.
@@ -1132,13 +1110,11 @@ static hipError_t launch_t(const IndexerArgs &a, int target_wgs, hipStream_t st)
     }
   }
   if constexpr (HI == dk::HI && DI == dk::DI && ROWS < 8) {
-    // decode batches: register-streamed tiles, one wave per unit of the balanced split
-    if (a.slot.page_table == nullptr || a.slot.page_shift >= 5) {
-      // one row a wave: two waves a SIMD, three FP8 (two bf16) tiles in the ring; two rows a wave (their Q, w and
-      // two accumulator sets): one wave a SIMD, two tiles in the ring (deeper rings spill)
-      if constexpr (ROWS == 1) return launch_decode<FP8, 1, 8, FP8 ? 3 : 2>(a, target_wgs * 8, st);
-      else return launch_decode<FP8, ROWS, 4, 2>(a, target_wgs * 4, st);
-    }
+    // decode batches: register-streamed tiles, one wave per unit of the balanced split. One row a wave: two waves
+    // a SIMD, three FP8 (two bf16) tiles in the ring; two rows a wave (their Q, w and two accumulator sets): one
+    // wave a SIMD, two tiles in the ring (deeper rings spill)
+    if constexpr (ROWS == 1) return launch_decode<FP8, 1, 8, FP8 ? 3 : 2>(a, target_wgs * 8, st);
+    else return launch_decode<FP8, ROWS, 4, 2>(a, target_wgs * 4, st);
   }
   const Split sp = key_split(a.max_kv_len, C::BK, row_blocks, target_wgs);
   const int chunks = sp.chunks, bpc = sp.bpc;

@@ -1,7 +1,7 @@
 """Edge cases of the register-streamed decode indexer (one or two query rows a wave), through the C ABI (MI355X
-only): two-row blocks that straddle two sequences (three queries per sequence), pages of 32, 64 and 128 keys (and
-16, which the staged kernel serves), positions on and around the 32-key tile boundaries, sequences shorter than a
-tile, bf16 and FP8 keys. Every score 0..p of every row is checked against the oracle at the indexer tolerance, and
+only): two-row blocks that straddle two sequences (three queries per sequence), pages of 16, 32, 64 and 128 keys
+(pages shorter than a 32-key tile put one tile's keys on several pages), positions on and around the tile
+boundaries, sequences shorter than a tile, bf16 and FP8 keys. Every score 0..p of every row is checked against the oracle at the indexer tolerance, and
 every entry past p must keep the fill value (the stores past a row's position are dropped, never written)."""
 
 import numpy as np
