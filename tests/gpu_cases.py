@@ -11,7 +11,7 @@ import torch
 
 import dsa_lightning_indexer_02_amd as dsa
 import oracle
-from workloads import bits_u16, bits_u8
+from workloads import bits_u16, bits_u8, fp8_encode_rows
 
 DEV = "cuda"
 
@@ -101,5 +101,38 @@ def log(msg):
     say(msg)
 
 
+def decode_batch(seed, lens, news, fp8, page, H_I=64, D_I=128):
+    """A seeded decode-style batch as host arrays and tensors: lens[b] cached tokens per sequence, the last
+    news[b] of them queries; page = None for a contiguous cache, else pages of that many tokens in a seeded
+    random physical order; FP8 keys (raw N(0,1), per-token scale) or bf16 keys N(0,1)/sqrt(d_I)."""
+    rng = np.random.default_rng(seed)
+    num_seqs, max_kv = len(lens), max(lens)
+    q_seq = np.array([b for b in range(num_seqs) for _ in range(news[b])], dtype=np.int32)
+    q_pos = np.array([lens[b] - news[b] + i for b in range(num_seqs) for i in range(news[b])], dtype=np.int32)
+    n_q = len(q_pos)
+    if page is None:
+        stride = (max_kv + 63) // 64 * 64
+        slots, pt = num_seqs * stride, None
+    else:
+        stride = 0
+        n_pages = [(L + page - 1) // page for L in lens]
+        perm = rng.permutation(sum(n_pages)).astype(np.int32)
+        pt = np.zeros((num_seqs, max(n_pages)), dtype=np.int32)
+        off = 0
+        for b, npg in enumerate(n_pages):
+            pt[b, :npg] = perm[off: off + npg]
+            off += npg
+        slots = sum(n_pages) * page
+    raw = rng.standard_normal((slots, D_I)).astype(np.float32)
+    if fp8:
+        k_idx, k_scale = fp8_encode_rows(torch.from_numpy(raw))
+    else:
+        k_idx, k_scale = torch.from_numpy(raw / np.sqrt(D_I)).to(torch.bfloat16), None
+    q_idx = torch.from_numpy(rng.standard_normal((n_q, H_I, D_I)).astype(np.float32) / np.sqrt(D_I)).to(torch.bfloat16)
+    w = torch.from_numpy(rng.random((n_q, H_I)).astype(np.float32) / 8)
+    return dict(num_seqs=num_seqs, max_kv=max_kv, q_seq=q_seq, q_pos=q_pos, stride=stride, pt=pt, page=page,
+                k_idx=k_idx, k_scale=k_scale, q_idx=q_idx, w=w, fp8=fp8)
+
+
 __all__ = ["say", "ld_for", "on_device", "batch_of", "oracle_scores", "indexer_rel_err", "run_indexer",
-           "check_attn", "attn_oracle", "bf16_to_f64", "spread_rows", "math"]
+           "check_attn", "attn_oracle", "bf16_to_f64", "spread_rows", "decode_batch", "math"]

@@ -10,45 +10,11 @@ import torch
 
 import dsa_lightning_indexer_02_amd as dsa
 import oracle
-from workloads import bits_u16, bits_u8, fp8_encode_rows
+from workloads import bits_u16, bits_u8
 
-from gpu_cases import DEV, indexer_rel_err, ld_for, say
+from gpu_cases import DEV, decode_batch, indexer_rel_err, ld_for, say
 
 pytestmark = pytest.mark.gpu
-
-H_I, D_I = 64, 128
-
-
-def _batch(seed, lens, news, fp8, page):
-    """lens[b] cached tokens per sequence, the last news[b] of them queries; page = None for a contiguous cache."""
-    rng = np.random.default_rng(seed)
-    num_seqs, max_kv = len(lens), max(lens)
-    q_seq = np.array([b for b in range(num_seqs) for _ in range(news[b])], dtype=np.int32)
-    q_pos = np.array([lens[b] - news[b] + i for b in range(num_seqs) for i in range(news[b])], dtype=np.int32)
-    n_q = len(q_pos)
-    if page is None:
-        stride = (max_kv + 63) // 64 * 64
-        slots, pt = num_seqs * stride, None
-    else:
-        stride = 0
-        n_pages = [(L + page - 1) // page for L in lens]
-        perm = rng.permutation(sum(n_pages)).astype(np.int32)
-        pt = np.zeros((num_seqs, max(n_pages)), dtype=np.int32)
-        off = 0
-        for b, npg in enumerate(n_pages):
-            pt[b, :npg] = perm[off: off + npg]
-            off += npg
-        slots = sum(n_pages) * page
-    raw = rng.standard_normal((slots, D_I)).astype(np.float32)
-    if fp8:
-        k_idx, k_scale = fp8_encode_rows(torch.from_numpy(raw))
-    else:
-        k_idx, k_scale = torch.from_numpy(raw / np.sqrt(D_I)).to(torch.bfloat16), None
-    q_idx = torch.from_numpy(rng.standard_normal((n_q, H_I, D_I)).astype(np.float32) / np.sqrt(D_I)).to(torch.bfloat16)
-    w = torch.from_numpy(rng.random((n_q, H_I)).astype(np.float32) / 8)
-    return dict(num_seqs=num_seqs, max_kv=max_kv, q_seq=q_seq, q_pos=q_pos, stride=stride, pt=pt, page=page,
-                k_idx=k_idx, k_scale=k_scale, q_idx=q_idx, w=w, fp8=fp8)
-
 
 def _check(d, label):
     n_q, max_kv = len(d["q_pos"]), d["max_kv"]
@@ -86,21 +52,21 @@ LENS = [5000, 777, 3001, 64, 33, 32, 31, 2, 1, 97, 4096, 4097]
 @pytest.mark.parametrize("fp8,page", [(True, 64), (True, None), (False, None), (False, 32)])
 def test_three_rows_a_sequence(fp8, page):
     news = [min(3, L) for L in LENS]
-    _check(_batch(41, LENS, news, fp8, page), "three rows a sequence")
+    _check(decode_batch(41, LENS, news, fp8, page), "three rows a sequence")
 
 
 @pytest.mark.parametrize("page", [16, 32, 128])
 def test_page_sizes_one_row(page):
     lens = [9000, 129, 128, 127, 65, 1, 2050]
-    _check(_batch(43, lens, [1] * len(lens), True, page), f"one row a sequence, pages of {page}")
+    _check(decode_batch(43, lens, [1] * len(lens), True, page), f"one row a sequence, pages of {page}")
 
 
 @pytest.mark.parametrize("fp8,page", [(True, None), (False, 32), (False, None)])
 def test_tile_boundaries_one_row(fp8, page):
     lens = [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 4095, 4096, 4097]
-    _check(_batch(47, lens, [1] * len(lens), fp8, page), "positions around tile boundaries")
+    _check(decode_batch(47, lens, [1] * len(lens), fp8, page), "positions around tile boundaries")
 
 
 def test_two_rows_paged_bf16():
     lens = [20000, 7000, 300, 2]
-    _check(_batch(53, lens, [2] * len(lens), False, 64), "two rows a sequence, bf16 keys in pages of 64")
+    _check(decode_batch(53, lens, [2] * len(lens), False, 64), "two rows a sequence, bf16 keys in pages of 64")
