@@ -167,6 +167,19 @@ void sparse_attn_kernel(AttnArgs a, int keys_per_split) {
     const int i = e * C::NT + tid;
     ent[e] = i < nlist ? idx_row[i] : -1;
   }
+  // Paged caches (never OFF32): every entry's page id is loaded once the list has landed and before the Q loads
+  // go out (entries outside 0..p_r read the sequence's first page id, never used), so the slots wait for one
+  // page-table latency and not for Q; contiguous caches load nothing more here.
+  const bool paged = !OFF32 && a.slot.page_table != nullptr;
+  int pid[PE];
+  if (paged) {
+    const int32_t *ptab = a.slot.page_table + (int64_t)b * a.slot.max_pages;
+#pragma unroll
+    for (int e = 0; e < PE; ++e) {
+      const bool ok = ent[e] >= 0 && ent[e] <= p_r;
+      pid[e] = ptab[ok ? ent[e] >> a.slot.page_shift : 0];
+    }
+  }
   // Q^T fragments of this wave's 32 heads (B operand: column = head, 8 consecutive d per half-wave). The K
   // steps kept in LDS wait in q_tail until tile 0 has landed, so no wait for Q comes before the first gather:
   // the Q loads and the first tiles' gathers are in flight together.
@@ -181,12 +194,26 @@ void sparse_attn_kernel(AttnArgs a, int keys_per_split) {
     else q_tail[s - C::QR] = v;
   }
   uint32_t sl[PE];
+  if (paged) {
+    const int mask = (1 << a.slot.page_shift) - 1;
+#pragma unroll
+    for (int e = 0; e < PE; ++e) {
+      const bool ok = ent[e] >= 0 && ent[e] <= p_r;
+      sl[e] = ok ? (uint32_t)(((int64_t)pid[e] << a.slot.page_shift) + (ent[e] & mask)) : 0u;
+    }
+  } else {
+    const int64_t seq0 = (int64_t)b * a.slot.seq_stride;
+#pragma unroll
+    for (int e = 0; e < PE; ++e) {
+      const bool ok = ent[e] >= 0 && ent[e] <= p_r;
+      if constexpr (OFF32) sl[e] = ok ? (uint32_t)(seq0 + ent[e]) * (uint32_t)C::ROWB : 0u;
+      else sl[e] = ok ? (uint32_t)(seq0 + ent[e]) : 0u;
+    }
+  }
   uint64_t msk[PE];
 #pragma unroll
   for (int e = 0; e < PE; ++e) {
     const bool ok = ent[e] >= 0 && ent[e] <= p_r;
-    if constexpr (OFF32) sl[e] = ok ? (uint32_t)a.slot(b, ent[e]) * (uint32_t)C::ROWB : 0u;
-    else sl[e] = ok ? (uint32_t)a.slot(b, ent[e]) : 0u;
     msk[e] = ballot(ok);
     if (lane == 0) lds_cnt[e * C::NWAVE + wv] = (uint32_t)__popcll(msk[e]);
   }
