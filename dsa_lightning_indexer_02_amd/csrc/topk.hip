@@ -752,12 +752,20 @@ __global__ __launch_bounds__(W * kWave) void topk_wchunk_kernel(const float *__r
   // the row length first: the sample loads below depend on it and need not wait behind the chunk's loads
   const int n = q_pos[r] + 1;
   f32x4 x[V];
+  if (vec) {
+    // ld and the chunk's start are multiples of 4, so a lane's four keys lie all inside the allocation or all
+    // past it (avail >= 4): every lane loads, past the end the allocation's last four keys, which are never used
+    // (positions past the row's length are masked below, and len <= avail). No branch or use separates the loads
+    // from the sample's, so all of them are in flight together.
 #pragma unroll
-  for (int u = 0; u < V; ++u) {
-    const int L = wbase + u * 4 * kWave + 4 * lane;
-    if (vec && L + 3 < avail) {
-      x[u] = *(const f32x4 *)(crow + L);
-    } else {
+    for (int u = 0; u < V; ++u) {
+      const int L = wbase + u * 4 * kWave + 4 * lane;
+      x[u] = *(const f32x4 *)(crow + min(L, avail - 4));
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      const int L = wbase + u * 4 * kWave + 4 * lane;
       x[u].x = L + 0 < avail ? crow[L + 0] : 0.f;
       x[u].y = L + 1 < avail ? crow[L + 1] : 0.f;
       x[u].z = L + 2 < avail ? crow[L + 2] : 0.f;
