@@ -35,12 +35,14 @@ __global__ __launch_bounds__(kTopkBlock) void topk_rows_kernel(const float *__re
     return;
   }
   const float *row = scores + (int64_t)r * ld;
+  // every item loads (past the row's end the row's last score, replaced below) so that no branch separates
+  // the loads: they go out together and the row pays one memory latency
+  float v[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) v[i] = row[min(i * kTopkBlock + (int)threadIdx.x, n - 1)];
   uint32_t key[ITEMS];
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int L = i * kTopkBlock + threadIdx.x;
-    key[i] = L < n ? order_key(row[L]) : 0u;
-  }
+  for (int i = 0; i < ITEMS; ++i) key[i] = i * kTopkBlock + (int)threadIdx.x < n ? order_key(v[i]) : 0u;
   select_topk<ITEMS>(key, n, k, [&](int rank, int L, uint32_t) { out[rank] = L; }, sh);
 }
 
