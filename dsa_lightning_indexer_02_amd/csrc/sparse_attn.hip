@@ -532,12 +532,15 @@ void sparse_attn_kernel(AttnArgs a, int keys_per_split) {
 
 // Merge of the split partials: out = sum_j w_j Obar_j with w_j = 2^(m_j - M) l_j / L, L = sum_j 2^(m_j - M) l_j,
 // M = max_j m_j over the splits that saw a key (l_j > 0), Obar_j the split's own softmax output (bf16). One
-// workgroup = one row x HPW heads; a thread owns 16 consecutive outputs of one head, so its loads over the
-// splits are independent 32-byte reads the compiler can keep in flight.
+// workgroup = one row x HPW heads; a thread owns 16 consecutive outputs of one head. Splits are taken SB at a
+// time and every load of a batch goes out before any is used (indexes past the last split repeat it and are
+// weighted 0), so up to SB splits cost one memory latency: (m, l) and the partial rows together when the row
+// has at most SB splits, else one pass over (m, l) for M and one over the batches.
 template <int DV>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int TPH = DV / 16;          // threads per head
   constexpr int HPW = 256 / TPH;        // heads per workgroup
+  constexpr int SB = 8;                 // splits per batch of loads
   static_assert(DV % 16 == 0 && 256 % TPH == 0, "combine tiling");
   const int groups = (a.H + HPW - 1) / HPW;
   const int r = blockIdx.x / groups;
@@ -546,29 +549,51 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   if (h >= a.H) return;
   const int S = a.splits;
   const float *ml = a.ws + sparse_attn_ws_ml_offset(a.num_q, S, a.H, DV);   // [num_q, splits, H, 2]: (m, l)
+  const f32x2 *mlh = (const f32x2 *)ml + (int64_t)r * S * a.H + h;          // split j at mlh[j * H]
+  const u32x4 *poh = (const u32x4 *)((const uint16_t *)a.ws + ((int64_t)r * S * a.H + h) * DV + d0);
+  const int64_t pstride = (int64_t)a.H * DV / 8;                            // u32x4 per split
   float M = -INFINITY;
-  for (int j = 0; j < S; ++j) {
-    const f32x2 v = *(const f32x2 *)(ml + (((int64_t)r * S + j) * a.H + h) * 2);
-    if (v.y > 0.f) M = fmaxf(M, v.x);
+  if (S > SB) {
+    for (int j0 = 0; j0 < S; j0 += SB) {
+      f32x2 v[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) v[u] = mlh[(int64_t)min(j0 + u, S - 1) * a.H];
+#pragma unroll
+      for (int u = 0; u < SB; ++u)
+        if (j0 + u < S && v[u].y > 0.f) M = fmaxf(M, v[u].x);
+    }
   }
   float L = 0.f;
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll 4
-  for (int j = 0; j < S; ++j) {
-    const f32x2 v = *(const f32x2 *)(ml + (((int64_t)r * S + j) * a.H + h) * 2);
-    const float f = v.y > 0.f ? exp2f(v.x - M) * v.y : 0.f;   // an empty split has weight 0
-    L += f;
-    const u32x4 *po = (const u32x4 *)((const uint16_t *)a.ws + (((int64_t)r * S + j) * a.H + h) * DV + d0);
+  for (int j0 = 0; j0 < S; j0 += SB) {
+    f32x2 v[SB];
+    u32x4 w[SB][2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const u32x4 w = po[q];
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    for (int u = 0; u < SB; ++u) {
+      const int j = min(j0 + u, S - 1);
+      v[u] = mlh[(int64_t)j * a.H];
+      w[u][0] = poh[j * pstride];
+      w[u][1] = poh[j * pstride + 1];
+    }
+    if (S <= SB) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[q * 8 + 2 * e] = fmaf(f, bf16_lo(ww[e]), acc[q * 8 + 2 * e]);
-        acc[q * 8 + 2 * e + 1] = fmaf(f, bf16_hi(ww[e]), acc[q * 8 + 2 * e + 1]);
+      for (int u = 0; u < SB; ++u)
+        if (u < S && v[u].y > 0.f) M = fmaxf(M, v[u].x);
+    }
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const float f = j0 + u < S && v[u].y > 0.f ? exp2f(v[u].x - M) * v[u].y : 0.f;   // an empty split weighs 0
+      L += f;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t ww[4] = {w[u][q].x, w[u][q].y, w[u][q].z, w[u][q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[q * 8 + 2 * e] = fmaf(f, bf16_lo(ww[e]), acc[q * 8 + 2 * e]);
+          acc[q * 8 + 2 * e + 1] = fmaf(f, bf16_hi(ww[e]), acc[q * 8 + 2 * e + 1]);
+        }
       }
     }
   }

@@ -67,13 +67,37 @@ __global__ __launch_bounds__(kTopkBlock) void topk_merge_kernel(const int32_t *_
   const int last_len = n - (used - 1) * chunk;
   const int total = (used - 1) * k + min(last_len, k);
   const int64_t base = (int64_t)r * n_chunks * k;
+  // Up to 32 items a thread, keys and positions load together and branch-free, as in the rows form (past the
+  // last candidate the last one is loaded, then replaced), and the output pass only stores (item i is
+  // L = i * kTopkBlock + tid). At 64 the positions would not fit in registers beside the keys (and the clamped
+  // addresses spill): the keys load masked and the positions are read per output.
+  constexpr bool kPosInRegs = ITEMS <= 32;
   uint32_t key[ITEMS];
+  int32_t pos[kPosInRegs ? ITEMS : 1];
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    const int L = i * kTopkBlock + threadIdx.x;
-    key[i] = L < total ? cand_key[base + L] : 0u;
+    const int L = i * kTopkBlock + (int)threadIdx.x;
+    if constexpr (kPosInRegs) {
+      const int64_t c = base + min(L, total - 1);
+      key[i] = cand_key[c];
+      pos[i] = cand_pos[c];
+    } else {
+      key[i] = L < total ? cand_key[base + L] : 0u;
+    }
   }
-  select_topk<ITEMS>(key, total, k, [&](int rank, int L, uint32_t) { out[rank] = cand_pos[base + L]; }, sh);
+  if constexpr (kPosInRegs) {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) key[i] = i * kTopkBlock + (int)threadIdx.x < total ? key[i] : 0u;
+  }
+  select_topk<ITEMS>(
+      key, total, k,
+      [&](int rank, int L, uint32_t) {
+        if constexpr (kPosInRegs)
+          out[rank] = pos[(L - (int)threadIdx.x) / kTopkBlock];
+        else
+          out[rank] = cand_pos[base + L];
+      },
+      sh);
 }
 
 // ---------------------------------------------------------------------------------------------------------
