@@ -873,8 +873,11 @@ __global__ __launch_bounds__(W * kWave) void topk_wmerge_kernel(const float *__r
   __shared__ StreamSharedT<W> sh;
   __shared__ uint32_t pre[kWMaxChunks + 1];
   const int r = blockIdx.x, tid = threadIdx.x;
-  // the counts are loaded with q_pos (chunks past the row's end are masked once n is known)
+  // the counts and the row's window (written by chunk 0 of this row) are loaded with q_pos (chunks past the
+  // row's end are masked once n is known)
   const uint32_t v_raw = tid < n_chunks ? cand_cnt[(int64_t)r * n_chunks + tid] : 0u;
+  const uint32_t top = cand_cnt[(int64_t)gridDim.x * n_chunks + r];
+  const uint32_t lo = cand_cnt[(int64_t)gridDim.x * (n_chunks + 1) + r];
   const int n = q_pos[r] + 1;
   int32_t *out = idx + (int64_t)r * k;
   if (n <= k) {
@@ -933,8 +936,6 @@ __global__ __launch_bounds__(W * kWave) void topk_wmerge_kernel(const float *__r
   uint32_t ccs[W];
 #pragma unroll
   for (int i = 0; i < W; ++i) ccs[i] = (uint32_t)min(max((int)M - i * CPW, 0), CPW);
-  const uint32_t top = cand_cnt[(int64_t)gridDim.x * n_chunks + r];          // written by chunk 0 of this row
-  const uint32_t lo = cand_cnt[(int64_t)gridDim.x * (n_chunks + 1) + r];
   if (!window_select_emit(ccs, lo, top, (uint32_t)k, sh, emit)) {
     int s0, s1;
     stream_segment_of<W>(n, s0, s1);
