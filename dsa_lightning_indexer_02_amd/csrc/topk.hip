@@ -332,16 +332,32 @@ __device__ __forceinline__ void stream_window(const float *__restrict__ row, int
 // ---- 2. one pass over this wave's segment [s0, s1): every key >= lo with its position goes to the wave's LDS
 //      region (position order; cc counts them all, only the first kCandPerWave are stored), and ca counts the
 //      keys above hi.
-__device__ __forceinline__ void stream_collect(const float *__restrict__ row, int s0, int s1, bool vec, uint32_t lo,
-                                               uint32_t hi, StreamShared &sh, uint32_t &ca, uint32_t &cc) {
-  const int w = threadIdx.x / kWave;
+// 16-byte form (rows 16-byte aligned): lane l takes positions L .. L+3, L = L0 + 4l (lane order is position
+// order), kCollectU loads per lane a batch. Loads are clamped to the segment's last aligned position (nothing
+// past the row is read; the positions past s1 are masked by their count), so a batch issues without a branch:
+// the caller loads the first batch before the window is known, and each step issues the next batch before
+// processing the current one, so the loads of a batch overlap the processing of the one before.
+constexpr int kCollectU = 4;
+__device__ __forceinline__ void stream_load4(const float *__restrict__ row, int L0, int s1, f32x4 (&v)[kCollectU]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int last = max(0, (s1 - 1) & ~3);
+#pragma unroll
+  for (int u = 0; u < kCollectU; ++u) v[u] = *(const f32x4 *)(row + min(L0 + u * 4 * kWave + 4 * lane, last));
+}
+
+__device__ __forceinline__ void stream_collect4(const float *__restrict__ row, int s0, int s1, uint32_t lo,
+                                                uint32_t hi, StreamShared &sh, f32x4 (&a)[kCollectU], uint32_t &ca,
+                                                uint32_t &cc) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int cb = w * kCandPerWave;
-  ca = 0u;
-  cc = 0u;
-  if (vec) {
-    uint32_t ca_lane = 0u;   // keys above the window, this lane's share
-    uint32_t ccl = 0u;
-    stream_segment4(row, s0, s1, [&](int L, const uint32_t (&x)[4], int nv) {
+  constexpr int STEP = 4 * kWave * kCollectU;
+  uint32_t ca_lane = 0u, ccl = 0u;
+  auto process = [&](int L0, const f32x4 (&v)[kCollectU]) {
+#pragma unroll
+    for (int u = 0; u < kCollectU; ++u) {
+      const int L = L0 + u * 4 * kWave + 4 * lane;
+      const int nv = min(4, max(0, s1 - L));
+      const uint32_t x[4] = {order_key(v[u].x), order_key(v[u].y), order_key(v[u].z), order_key(v[u].w)};
       uint32_t nc = 0u;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -363,25 +379,41 @@ __device__ __forceinline__ void stream_collect(const float *__restrict__ row, in
         }
       }
       ccl += tot;
-    });
-    ca = wave_sum_u32(ca_lane);
-    cc = ccl;
-  } else {
-    uint32_t cal = 0u, ccl = 0u;
-    stream_segment(row, s0, s1, [&](int L, uint32_t x, bool valid) {
-      cal += (uint32_t)__popcll(ballot(valid && x > hi));
-      const bool c = valid && x >= lo;
-      const uint64_t bm = ballot(c);
-      const uint32_t slot = ccl + (uint32_t)lanes_below(bm);
-      if (c && slot < (uint32_t)kCandPerWave) {
-        sh.cand_key[cb + slot] = x;
-        sh.cand_pos[cb + slot] = L;
-      }
-      ccl += (uint32_t)__popcll(bm);
-    });
-    ca = cal;
-    cc = ccl;
+    }
+  };
+  f32x4 b[kCollectU];
+  for (int L0 = s0; L0 < s1;) {   // two batches a trip, so the buffers swap roles without register copies
+    stream_load4(row, L0 + STEP, s1, b);
+    process(L0, a);
+    L0 += STEP;
+    if (L0 >= s1) break;
+    stream_load4(row, L0 + STEP, s1, a);
+    process(L0, b);
+    L0 += STEP;
   }
+  ca = wave_sum_u32(ca_lane);
+  cc = ccl;
+}
+
+// Element-wise form (any alignment).
+__device__ __forceinline__ void stream_collect(const float *__restrict__ row, int s0, int s1, uint32_t lo,
+                                               uint32_t hi, StreamShared &sh, uint32_t &ca, uint32_t &cc) {
+  const int w = threadIdx.x / kWave;
+  const int cb = w * kCandPerWave;
+  uint32_t cal = 0u, ccl = 0u;
+  stream_segment(row, s0, s1, [&](int L, uint32_t x, bool valid) {
+    cal += (uint32_t)__popcll(ballot(valid && x > hi));
+    const bool c = valid && x >= lo;
+    const uint64_t bm = ballot(c);
+    const uint32_t slot = ccl + (uint32_t)lanes_below(bm);
+    if (c && slot < (uint32_t)kCandPerWave) {
+      sh.cand_key[cb + slot] = x;
+      sh.cand_pos[cb + slot] = L;
+    }
+    ccl += (uint32_t)__popcll(bm);
+  });
+  ca = cal;
+  cc = ccl;
 }
 
 // Output slots of the kept keys: keys > T, and the first need_eq T-valued keys in position order (wave order,
@@ -684,10 +716,16 @@ __global__ __launch_bounds__(kStreamThreads) void topk_stream_kernel(const float
   const bool vec = (ld & 3) == 0 && ((uintptr_t)scores & 15) == 0;
   int s0, s1;
   stream_segment_of(n, s0, s1);
+  // the first batch of the segment goes out with the sample: one memory latency for both
+  f32x4 a[kCollectU];
+  if (vec) stream_load4(row, s0, s1, a);
   uint32_t lo, hi;
   stream_window(row, n, k, sh, lo, hi);
   uint32_t ca, cc;
-  stream_collect(row, s0, s1, vec, lo, hi, sh, ca, cc);
+  if (vec)
+    stream_collect4(row, s0, s1, lo, hi, sh, a, ca, cc);
+  else
+    stream_collect(row, s0, s1, lo, hi, sh, ca, cc);
   uint32_t ccs[kStreamWaves], c_above, c_cand;
   bool fits;
   stream_counts(ca, cc, sh, ccs, c_above, c_cand, fits);
