@@ -116,6 +116,22 @@ def test_stream_gaussian_long_rows():
     _run(s, pos, 2048, "stream gaussian")
 
 
+def test_stream_segment_and_batch_boundaries():
+    """The streaming form's pass over the row: each of the 4 waves walks a segment of ceil(n / 4) positions rounded
+    up to 256, in steps of 1,024 positions (four 16-byte loads a lane), loads clamped to the segment's last
+    aligned position. Row lengths whose segments end exactly on a step, one past it, one short of it, and whose
+    last wave's segment is a few positions long or empty must come out exact."""
+    rng = np.random.default_rng(21)
+    n_q, max_kv = 520, 20000
+    s = _mk(n_q, max_kv, lambda n, g: g.standard_normal(n).astype(np.float32), rng)
+    lengths = [8192, 8193, 8191, 12288, 12289, 12287, 16384, 16385, 16383, 9216, 9217, 10240, 11264, 8448, 8449,
+               12292, 12291, 16388, 19968, 19999, 20000, 2049, 2305, 2306, 3073, 3075, 4097]
+    pos = rng.integers(8192, max_kv, n_q)
+    for i, n in enumerate(lengths):
+        pos[i] = n - 1
+    _run(s, pos, 2048, "stream segment/batch boundaries")
+
+
 def test_stream_window_miss_falls_back():
     # the sample reads 64 runs of 64 keys starting at floor(b * (n - 64) / 63); put the k + 100 largest keys
     # elsewhere, so every sampled key is 0 and the window cannot hold the k-th key
