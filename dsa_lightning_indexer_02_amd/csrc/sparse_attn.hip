@@ -535,12 +535,12 @@ void sparse_attn_kernel(AttnArgs a, int keys_per_split) {
 // workgroup = one row x HPW heads; a thread owns 16 consecutive outputs of one head. Splits are taken SB at a
 // time and every load of a batch goes out before any is used (indexes past the last split repeat it and are
 // weighted 0), so up to SB splits cost one memory latency: (m, l) and the partial rows together when the row
-// has at most SB splits, else one pass over (m, l) for M and one over the batches.
-template <int DV>
+// has at most SB splits, else one pass over (m, l) for M and one over the batches. The launch picks the
+// smallest SB of 2, 4, 8 that holds the row's splits, so no load repeats another when they fit one batch.
+template <int DV, int SB>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int TPH = DV / 16;          // threads per head
   constexpr int HPW = 256 / TPH;        // heads per workgroup
-  constexpr int SB = 8;                 // splits per batch of loads
   static_assert(DV % 16 == 0 && 256 % TPH == 0, "combine tiling");
   const int groups = (a.H + HPW - 1) / HPW;
   const int r = blockIdx.x / groups;
@@ -632,7 +632,13 @@ static hipError_t launch_t(const AttnArgs &a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   constexpr int HPW = 256 / (DV / 16);
-  hipLaunchKernelGGL(attn_combine_kernel<DV>, dim3(a.num_q * ((a.H + HPW - 1) / HPW)), dim3(256), 0, st, a);
+  const dim3 grid(a.num_q * ((a.H + HPW - 1) / HPW));
+  if (a.splits <= 2)
+    hipLaunchKernelGGL((attn_combine_kernel<DV, 2>), grid, dim3(256), 0, st, a);
+  else if (a.splits <= 4)
+    hipLaunchKernelGGL((attn_combine_kernel<DV, 4>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<DV, 8>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
