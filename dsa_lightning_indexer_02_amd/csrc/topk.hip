@@ -119,7 +119,6 @@ __global__ __launch_bounds__(kTopkBlock) void topk_merge_kernel(const int32_t *_
 constexpr int kStreamWaves = 4;
 constexpr int kStreamThreads = kStreamWaves * kWave;
 constexpr int kStreamUnroll = 16;          // loads in flight per wave
-constexpr int kStreamUnroll4 = 8;          // 16-byte loads in flight per wave (aligned rows)
 constexpr int kRun = kWave;                // sample runs of 64 consecutive keys
 constexpr int kRuns = 64;
 constexpr int kSample = kRuns * kRun;      // 4096 sampled keys per row
@@ -237,29 +236,6 @@ __device__ __forceinline__ void stream_segment(const float *__restrict__ row, in
     for (int u = 0; u < kStreamUnroll; ++u) {
       const int L = L0 + u * kWave + lane;
       f(L, order_key(v[u]), L < s1);
-    }
-  }
-}
-
-// The same walk with 16-byte loads (rows 16-byte aligned, segment starts multiples of 4): lane l takes the 4
-// consecutive positions L .. L+3, L = L0 + 4l, so lane order is still position order. f(L, key[4], nv) is
-// called with nv = the number of those positions below s1 (0..4).
-template <class F>
-__device__ __forceinline__ void stream_segment4(const float *__restrict__ row, int s0, int s1, F f) {
-  const int lane = threadIdx.x & (kWave - 1);
-  constexpr int U = kStreamUnroll4;
-  for (int L0 = s0; L0 < s1; L0 += 4 * kWave * U) {
-    f32x4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int L = L0 + u * 4 * kWave + 4 * lane;
-      v[u] = L < s1 ? *(const f32x4 *)(row + L) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int L = L0 + u * 4 * kWave + 4 * lane;
-      const uint32_t x[4] = {order_key(v[u].x), order_key(v[u].y), order_key(v[u].z), order_key(v[u].w)};
-      f(L, x, min(4, max(0, s1 - L)));
     }
   }
 }
